@@ -1,0 +1,322 @@
+"""Plain fp64 CPU oracle for one rank's share of a fused GEMM + reduce-scatter.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant with the HIP library; it takes plain numpy arrays of bf16 bit
+patterns (``uint16``) and returns numpy arrays.
+
+What it computes, and where the pages define it
+-----------------------------------------------
+Sources are three web pages, cited by title and section:
+
+[PK]  "ParallelKittens: Systematic and Practical Simplification of Multi-GPU AI
+      Kernels" (paper summary page), section 3 "Technical Approach":
+      "Scheduling Analysis" (the fused GEMM + reduce-scatter example: every
+      GPU produces a partial of each output tile and the GPU owning that
+      tile's shard ends with the sum of all partials) and "The Eight PK
+      Primitives" (store_add_async adds a tile into the owner's buffer;
+      signal adds to a barrier word, wait spins until it reaches a value).
+[PKN] "ParallelKittens: Three Principles and Eight Primitives for Multi-GPU
+      Kernels" (reading notes), section 3 "Principle 2": the M x N x K
+      GEMM + reduce-scatter on P GPUs with bf16 elements (s = 2 bytes).
+[SYN] "Syncopate: Efficient Multi-GPU AI Kernels via Automatic Chunk-Centric
+      Compute-Communication Overlap", section 5.1 "Communication Schedule
+      Abstraction": a chunk is a logical block of one or more tiles that is
+      communicated as a unit.
+
+Definition implemented (one rank ``rank`` of ``P``; S = M / P):
+
+    C          = A . B                       (this rank's local partial, M x N)
+    send[j]    = bf16_rne(C[d*S:(d+1)*S, :])  for every destination d != rank,
+                                              slot j = d if d < rank else d - 1
+    out        = C[rank*S:(rank+1)*S, :] + sum_j peers[j]   (j ascending)
+    ready[j,c] = 1, counter[j,c] = 0          for every slot j and chunk c
+
+The pages fix the mathematics (the owner ends with the sum over all ranks of
+their partials for its shard) but not the buffer layout, the rounding mode of
+the bf16 send copy, or the flag words; the readings taken here are:
+
+* shards are contiguous row blocks and rank r owns rows [r*S, (r+1)*S);
+* send buffers are bf16, rounded to nearest-even directly from the exact
+  (fp64) value -- no intermediate fp32 rounding;
+* slots skip the calling rank and are in ascending rank order;
+* chunk c of a slot is rows [c*chunk_rows, (c+1)*chunk_rows) of that slot, at
+  full width N;
+* the owned shard sums the staged peer partials in ascending slot order;
+* after the call every chunk's ready word is exactly 1 and its arrival
+  counter is back to 0.
+
+Everything is computed in fp64.  The matrix product is a library primitive
+(numpy ``matmul`` in float64); every other step is written out here.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "f64_to_bf16_bits",
+    "ulp_bf16",
+    "slot_of_dest",
+    "dest_of_slot",
+    "local_partial",
+    "local_partial_abs",
+    "reduce_scatter_share",
+    "gemm_rs_oracle",
+    "gemm_rs_elements",
+    "error_bound",
+    "OracleResult",
+]
+
+# ---------------------------------------------------------------------------
+# bf16 <-> fp64, from the IEEE-754 binary format definition.
+# bf16 = 1 sign bit, 8 exponent bits (bias 127), 7 stored fraction bits: the
+# top 16 bits of an IEEE binary32.  Smallest normal 2**-126, subnormal
+# spacing 2**-133, largest finite (2 - 2**-7) * 2**127.
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float64.
+
+    A bf16 pattern is the high half of the binary32 with the same value, so
+    shifting it up 16 bits and reinterpreting as float32 is exact; float32 ->
+    float64 is exact too.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):          # NaN patterns stay NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (float64 result).
+
+    For |x| in [2**E, 2**(E+1)) the spacing is 2**(E-7); below the smallest
+    normal 2**-126 it is the subnormal spacing 2**-133.
+    """
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(a)                   # a = m * 2**e, m in [0.5, 1)
+    E = np.where(a > 0, e - 1, -126)
+    E = np.maximum(E, -126)
+    return np.ldexp(np.ones_like(a), (E - 7).astype(np.int64))
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16, round-to-nearest-even, return uint16 bits.
+
+    Rounds once, directly from the float64 value: the result is the bf16
+    number nearest to x, ties going to the one whose last stored fraction bit
+    is 0.  Values whose rounded magnitude reaches 2**128 become infinity (the
+    IEEE overflow rule for round-to-nearest); NaN maps to the quiet NaN 0x7FC0
+    with the input's sign.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    q = ulp_bf16(a)                       # power of two: a / q is exact
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.rint(a / q) * q            # numpy rint: ties to even integer
+    r = np.where(r >= 2.0 ** 128, np.inf, r)
+    r = np.where(np.isinf(a), np.inf, r)
+    v = np.copysign(r, x)                 # keeps the sign of zero
+    # v is a bf16 value, hence exactly a float32; its top half is the pattern.
+    with np.errstate(invalid="ignore"):
+        f32 = v.astype(np.float32)
+    bits = (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if np.any(nan):
+        sign = (np.signbit(x).astype(np.uint16) << np.uint16(15))
+        bits = np.where(nan, np.uint16(0x7FC0) | sign, bits).astype(np.uint16)
+    return bits
+
+
+# ---------------------------------------------------------------------------
+# Slot / chunk bookkeeping (the readings listed in the module docstring).
+# ---------------------------------------------------------------------------
+
+
+def slot_of_dest(dest: int, rank: int) -> int:
+    """Send slot that holds the rows destined to rank ``dest`` (dest != rank)."""
+    if dest == rank:
+        raise ValueError("the owned shard has no send slot")
+    return dest if dest < rank else dest - 1
+
+
+def dest_of_slot(slot: int, rank: int) -> int:
+    """Inverse of :func:`slot_of_dest`."""
+    return slot if slot < rank else slot + 1
+
+
+# ---------------------------------------------------------------------------
+# The local partial and the reduce-scatter share.
+# ---------------------------------------------------------------------------
+
+
+def local_partial(A_bits: np.ndarray, B_bits: np.ndarray) -> np.ndarray:
+    """C = A . B in float64 (library matmul), from bf16 bit patterns.
+
+    [PKN] section 3: the local M x N x K GEMM whose output tiles are then sent
+    to their owners.  Products of two bf16 numbers are exact in float64; the
+    sums carry float64 rounding only.
+    """
+    A = bf16_bits_to_f64(A_bits)
+    B = bf16_bits_to_f64(B_bits)
+    if A.shape[1] != B.shape[0]:
+        raise ValueError("inner dimensions differ")
+    if A.shape[1] == 0:
+        return np.zeros((A.shape[0], B.shape[1]), dtype=np.float64)
+    return A @ B
+
+
+def local_partial_abs(A_bits: np.ndarray, B_bits: np.ndarray) -> np.ndarray:
+    """T = |A| . |B| in float64, the magnitude that scales rounding error."""
+    A = np.abs(bf16_bits_to_f64(A_bits))
+    B = np.abs(bf16_bits_to_f64(B_bits))
+    if A.shape[1] == 0:
+        return np.zeros((A.shape[0], B.shape[1]), dtype=np.float64)
+    return A @ B
+
+
+@dataclass
+class OracleResult:
+    send_bits: np.ndarray      # uint16 [P-1, S, N]   bf16 send buffers
+    out: np.ndarray            # float64 [S, N]       owned shard, exact sum
+    ready: np.ndarray          # uint32 [P-1, S/chunk_rows]
+    counters: np.ndarray       # uint32 [P-1, S/chunk_rows]
+    C: np.ndarray              # float64 [M, N]       local partial
+
+    @property
+    def flags(self) -> np.ndarray:
+        """Flag words in device order: all ready words, then all counters."""
+        return np.concatenate([self.ready.ravel(), self.counters.ravel()])
+
+    def out_bf16_bits(self) -> np.ndarray:
+        return f64_to_bf16_bits(self.out)
+
+    def out_f32(self) -> np.ndarray:
+        """The owned shard rounded once to float32 (nearest-even)."""
+        return self.out.astype(np.float32)
+
+
+def reduce_scatter_share(C: np.ndarray, peers: np.ndarray, P: int, rank: int,
+                         chunk_rows: int) -> OracleResult:
+    """Reduce-scatter share of rank ``rank`` given its local partial C.
+
+    [PK] "Scheduling Analysis": each output row block goes to the rank that
+    owns it; the owner adds every rank's partial for its shard.  ``peers``
+    (float64 [P-1, S, N]) are the partials that the other ranks sent to this
+    rank, slot j coming from rank dest_of_slot(j).  [SYN] 5.1: each slot is
+    split into chunks of ``chunk_rows`` full-width rows, each a unit whose
+    readiness is signalled once.
+    """
+    M, N = C.shape
+    if P < 1 or not (0 <= rank < P):
+        raise ValueError("need P >= 1 and 0 <= rank < P")
+    if M % P:
+        raise ValueError("M must be a multiple of P")
+    S = M // P
+    if chunk_rows <= 0 or (S % chunk_rows):
+        raise ValueError("chunk_rows must divide the shard height")
+    peers = np.asarray(peers, dtype=np.float64)
+    if peers.shape != (P - 1, S, N):
+        raise ValueError(f"peers must have shape {(P - 1, S, N)}")
+
+    send = np.empty((P - 1, S, N), dtype=np.uint16)
+    for d in range(P):
+        if d == rank:
+            continue
+        send[slot_of_dest(d, rank)] = f64_to_bf16_bits(C[d * S:(d + 1) * S, :])
+
+    out = C[rank * S:(rank + 1) * S, :].copy()
+    for j in range(P - 1):                # ascending slot order
+        out = out + peers[j]
+
+    n_chunks = S // chunk_rows
+    ready = np.ones((P - 1, n_chunks), dtype=np.uint32)
+    counters = np.zeros((P - 1, n_chunks), dtype=np.uint32)
+    return OracleResult(send_bits=send, out=out, ready=ready, counters=counters, C=C)
+
+
+def gemm_rs_oracle(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits: np.ndarray,
+                   P: int, rank: int, chunk_rows: int) -> OracleResult:
+    """Whole share from bf16 inputs: local partial, send copies, owned sum, flags."""
+    C = local_partial(A_bits, B_bits)
+    peers = bf16_bits_to_f64(peer_bits)
+    return reduce_scatter_share(C, peers, P, rank, chunk_rows)
+
+
+def gemm_rs_elements(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits, P: int,
+                     rank: int, rows: np.ndarray, cols: np.ndarray):
+    """Expected values at the output positions (rows[i], cols[i]) only.
+
+    For problems too large for the full product: each requested element of C
+    is its own fp64 dot product of one row of A and one column of B.  ``rows``
+    are global row indices in [0, M).  Returns ``(kind, value, mag)`` where
+    kind is 1 for rows in the owned shard (value = exact owned sum) and 0 for
+    rows that are sent (value = exact C, to be rounded by the caller), and mag
+    is |A|.|B| + sum_j |peer_j| at that position (for the rounding bound).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    M = A_bits.shape[0]
+    S = M // P
+    A = bf16_bits_to_f64(np.asarray(A_bits)[rows, :])            # [n, K]
+    Bc = bf16_bits_to_f64(np.asarray(B_bits)[:, cols]).T          # [n, K]
+    val = np.einsum("ik,ik->i", A, Bc)
+    mag = np.einsum("ik,ik->i", np.abs(A), np.abs(Bc))
+    owned = (rows // S) == rank
+    kind = owned.astype(np.int64)
+    if np.any(owned):
+        lr = rows[owned] - rank * S
+        lc = cols[owned]
+        acc = val[owned]
+        amag = mag[owned]
+        for j in range(P - 1):
+            pv = bf16_bits_to_f64(np.asarray(peer_bits[j])[lr, lc])
+            acc = acc + pv
+            amag = amag + np.abs(pv)
+        val = val.copy()
+        mag = mag.copy()
+        val[owned] = acc
+        mag[owned] = amag
+    return kind, val, mag
+
+
+# ---------------------------------------------------------------------------
+# Rounding bound for a float32-accumulating implementation.
+# ---------------------------------------------------------------------------
+
+
+def error_bound(mag: np.ndarray, n_terms: int, bf16_out: bool, ref: np.ndarray,
+                u: float = 2.0 ** -23) -> np.ndarray:
+    """Per-element tolerance for a float32 evaluation of the same sums.
+
+    A sum of n_terms products evaluated in a working precision with unit
+    roundoff u, in any order, differs from the exact value by at most
+    gamma_n * sum|terms| with gamma_n = n*u / (1 - n*u) (Higham, "Accuracy and
+    Stability of Numerical Algorithms", 2nd ed., section 3.1).  u = 2**-23
+    (twice the float32 unit roundoff) also covers hardware accumulators that
+    round toward zero.  The tolerance is the larger of that bound and 2 bf16
+    ulps of the reference; a bf16-stored result adds half a bf16 ulp for its
+    final rounding.
+    """
+    n = float(n_terms)
+    gamma = n * u / (1.0 - n * u)
+    tol = gamma * np.asarray(mag, dtype=np.float64)
+    if bf16_out:
+        tol = tol + 0.5 * ulp_bf16(np.abs(ref) + tol)
+    return np.maximum(tol, 2.0 * ulp_bf16(ref))
+
+
+def rel_frobenius(a: np.ndarray, ref: np.ndarray) -> float:
+    """||a - ref||_F / ||ref||_F (0 when both vanish)."""
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = math.sqrt(float(np.sum(ref * ref)))
+    num = math.sqrt(float(np.sum((a - ref) ** 2)))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den
