@@ -1,0 +1,246 @@
+"""Benchmark of one GPU's share of the fused bf16 GEMM + reduce-scatter.
+
+One step = re-zero the chunk flags + one fused call (local GEMM, bf16 send
+chunks with ready flags, owned-shard sum of the staged peer partials) over
+one batch of synthetic inputs resident in HBM.  Prints ONE JSON line.
+
+Default workload: P = 8, rank 3, M = N = 4096, K = 512 (the HBM-bound,
+communication-dominant case), rotating buffer sets so the 256 MB
+last-level cache cannot serve the inputs.  The K = 4096 compute-bound case
+(M = N = 32768) is measured in the same run and reported under "secondary".
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM+RS TFLOP/s & epilogue GB/s per GPU; % of MFMA/HBM roofline"
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="comm_dominant")
+    p.add_argument("--tile-order", type=int, default=None)
+    p.add_argument("--chunk-rows", type=int, default=None)
+    p.add_argument("--config", type=int, default=0)
+    p.add_argument("--group-n", type=int, default=0)
+    p.add_argument("--max-workgroups", type=int, default=0)
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gemm-only", action="store_true")
+    p.add_argument("--sweep", action="store_true",
+                   help="large-K schedule sweep: chunk_rows x tile order, one JSON line each")
+    return p.parse_args()
+
+
+class BufferSet:
+    def __init__(self, w, seed, chunk_rows, torch, gen, pk):
+        dev = "cuda"
+        self.A, self.B, self.peers = gen.make_inputs(w, dev, seed=seed)
+        self.send = torch.empty((w.P - 1, w.S, w.N), dtype=torch.bfloat16, device=dev)
+        odt = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+        self.out = torch.empty((w.S, w.N), dtype=odt, device=dev)
+        self.flags = torch.zeros(pk.pk_flags_words(w.P, w.M, chunk_rows), dtype=torch.int32,
+                                 device=dev)
+        self.gemm_out = None
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in
+                   (self.A, self.B, self.peers, self.send, self.out))
+
+
+def time_steps(fn, n_sets, warmup, steps, torch):
+    """Run warmup + timed steps; returns (ms per step, mean kernel ms)."""
+    for i in range(warmup):
+        fn(i % n_sets, None)
+    torch.cuda.synchronize()
+    ks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        fn((warmup + i) % n_sets, (ks[i], ke[i]))
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = t_start.elapsed_time(t_end) / steps
+    k_ms = sum(a.elapsed_time(b) for a, b in zip(ks, ke)) / steps
+    return ms_step, k_ms, wall
+
+
+def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_only=True,
+            tile_order=None, chunk_rows=None):
+    chunk = chunk_rows or args.chunk_rows or w.chunk_rows
+    order = w.tile_order if tile_order is None else tile_order
+    set_bytes = w.algorithmic_bytes()
+    n_sets = 1
+    if rotate and set_bytes < 2 * MALL_BYTES:
+        n_sets = max(2, min(8, math.ceil(1.2 * MALL_BYTES / set_bytes)))
+    sets = [BufferSet(w, 17 * i, chunk, torch, gen, pk) for i in range(n_sets)]
+    out_bf16 = 1 if w.out_dtype == "bf16" else 0
+    opts = dict(config=args.config, max_workgroups=args.max_workgroups, group_n=args.group_n)
+
+    def step(i, ev):
+        s = sets[i]
+        s.flags.zero_()
+        if ev:
+            ev[0].record()
+        pk.pk_gemm_rs_local_ex(s.A, s.B, s.peers, s.send, s.out, s.flags, w.M, w.N, w.K, w.P,
+                               w.rank, chunk, order, out_bf16, **opts)
+        if ev:
+            ev[1].record()
+
+    ms_step, k_ms, wall = time_steps(step, n_sets, warmup, steps, torch)
+    # every flag must be raised after the last call
+    assert all(int(s.flags[: s.flags.numel() // 2].min()) == 1 for s in sets)
+    res = dict(ms_per_step=ms_step, kernel_ms=k_ms, wall_s=wall, n_sets=n_sets,
+               chunk_rows=chunk, tile_order=order)
+    if gemm_only:
+        for s in sets:
+            s.gemm_out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+
+        def gstep(i, ev):
+            s = sets[i]
+            if ev:
+                ev[0].record()
+            pk.pk_gemm_rs_local_ex(s.A, s.B, None, None, s.gemm_out, None, w.M, w.N, w.K, w.P,
+                                   0, 0, 0, 1, gemm_only=True, **opts)
+            if ev:
+                ev[1].record()
+        _, g_ms, _ = time_steps(gstep, n_sets, warmup, steps, torch)
+        res["gemm_only_kernel_ms"] = g_ms
+        res["exposed_fraction"] = metrics.exposed_fraction(k_ms, g_ms)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline_of(w, kernel_ms, metrics):
+    if w.flops() / w.algorithmic_bytes() > metrics.PEAK_BF16_DENSE_FLOPS / metrics.PEAK_HBM_BYTES:
+        ach = w.flops() / (kernel_ms * 1e-3) / 1e12
+        peak = metrics.PEAK_BF16_DENSE_FLOPS / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None}
+    ach = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
+    peak = metrics.PEAK_HBM_BYTES / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": peak, "unit": "GB/s",
+            "frac": round(ach / peak, 4), "traffic": None}
+
+
+def cpu_baseline(w, gen, budget_s=12.0):
+    """The fp64 oracle on the host cores, on the full default share, repeated."""
+    import numpy as np  # noqa: F401
+    import oracle.gemm_rs_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    A, B, peers = gen.make_inputs(w, "cpu", seed=0)
+    Ab, Bb, Pb = gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.gemm_rs_oracle(Ab, Bb, Pb, w.P, w.rank, w.chunk_rows)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    per = el / n
+    return {"value": round(w.algorithmic_bytes() / per / 1e9, 3), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full oracle calls of the {w.name} share ({w.M}x{w.N}x{w.K}, P={w.P}), "
+                      f"{per:.3f} s each, fp64 numpy/OpenBLAS",
+            "tflops_fp64": round(w.flops() / per / 1e12, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU exchange is not part of this library)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from gemm_reduce_scatter_amd import binding as pk
+    from gemm_reduce_scatter_amd import inputs as gen
+    from gemm_reduce_scatter_amd import metrics
+
+    pk.load()
+    torch.cuda.init()
+    w = gen.WORKLOADS[args.workload]
+    if args.sweep:
+        w = gen.WORKLOADS["large_k"]
+        for chunk in w.sweep_chunk_rows:
+            for order in (0, 1, 2):
+                r = measure(w, args, torch, gen, pk, metrics, max(3, args.steps // 5), 2,
+                            rotate=False, gemm_only=False, tile_order=order, chunk_rows=chunk)
+                print(json.dumps({"workload": w.name, "chunk_rows": chunk, "tile_order": order,
+                                  "kernel_ms": round(r["kernel_ms"], 4),
+                                  "tflops": round(w.flops() / r["kernel_ms"] / 1e9, 1)}),
+                      flush=True)
+        return
+
+    r = measure(w, args, torch, gen, pk, metrics, args.steps, args.warmup,
+                gemm_only=not args.no_gemm_only)
+    roof = roofline_of(w, r["kernel_ms"], metrics)
+    cfg_id = args.config or pk.pk_select_config(w.M, w.N, w.K, w.P)
+    if roof["bound"] == "hbm":
+        value = w.algorithmic_bytes() / (r["ms_per_step"] * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        value = w.flops() / (r["ms_per_step"] * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "P": w.P, "rank": w.rank, "M": w.M, "N": w.N, "K": w.K,
+                   "chunk_rows": r["chunk_rows"], "tile_order": r["tile_order"],
+                   "out": w.out_dtype, "tile_config": pk.pk_config_info(cfg_id),
+                   "buffer_sets": r["n_sets"]},
+        "roofline": roof,
+        "kernel_ms": round(r["kernel_ms"], 5),
+        "tflops": round(w.flops() / (r["kernel_ms"] * 1e-3) / 1e12, 2),
+        "epilogue_gbps": round(w.epilogue_bytes() / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+    }
+    if "gemm_only_kernel_ms" in r:
+        line["gemm_only_kernel_ms"] = round(r["gemm_only_kernel_ms"], 5)
+        line["exposed_fraction"] = round(r["exposed_fraction"], 4)
+    if not args.no_secondary and args.workload != "compute_bound":
+        w2 = gen.WORKLOADS["compute_bound"]
+        r2 = measure(w2, args.__class__(**{**vars(args), "chunk_rows": None}), torch, gen, pk,
+                     metrics, max(5, args.steps // 5), 3, rotate=False,
+                     gemm_only=not args.no_gemm_only)
+        sec = {"workload": w2.name, "K": w2.K, "M": w2.M, "kernel_ms": round(r2["kernel_ms"], 4),
+               "tflops": round(w2.flops() / (r2["kernel_ms"] * 1e-3) / 1e12, 2),
+               "roofline": roofline_of(w2, r2["kernel_ms"], metrics)}
+        if "gemm_only_kernel_ms" in r2:
+            sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
+            sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, gen)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

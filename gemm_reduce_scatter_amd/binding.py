@@ -1,0 +1,208 @@
+"""ctypes binding of libpk_gemm_rs.so (declared in include/pk_gemm_rs.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, a negative return code becomes a
+:class:`PkError`.  Every step of the computation runs in the HIP library; if
+the library is missing this module raises instead of computing anything
+itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libpk_gemm_rs.so"
+_lib = None
+
+ROW_MAJOR, OWNED_FIRST, DEST_ROUND_ROBIN = 0, 1, 2
+
+
+class PkError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} (code {code})")
+        self.code = code
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("config", ctypes.c_int), ("max_workgroups", ctypes.c_int),
+                ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int)]
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load():
+    """Load the shared library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: run __graft_entry__.build() (hipcc, gfx950) first")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    main = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32]
+    lib.pk_gemm_rs_local.argtypes = main + [vp]
+    lib.pk_gemm_rs_local_bf16out.argtypes = main + [vp]
+    lib.pk_gemm_rs_local_ex.argtypes = main + [i32, ctypes.POINTER(_Options), vp]
+    for f in ("pk_gemm_rs_local", "pk_gemm_rs_local_bf16out", "pk_gemm_rs_local_ex"):
+        getattr(lib, f).restype = i32
+    lib.pk_flags_words.argtypes = [i32, i64, i32]
+    lib.pk_flags_words.restype = i64
+    lib.pk_validate.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32,
+                                ctypes.POINTER(_Options)]
+    lib.pk_validate.restype = i32
+    lib.pk_config_count.argtypes = []
+    lib.pk_config_count.restype = i32
+    ip = ctypes.POINTER(i32)
+    lib.pk_config_info.argtypes = [i32, ip, ip, ip, ip, ip, ip]
+    lib.pk_config_info.restype = i32
+    lib.pk_select_config.argtypes = [i64, i64, i64, i32]
+    lib.pk_select_config.restype = i32
+    lib.pk_tile_walk.argtypes = [i64, i64, i32, i32, i32, i32, i32,
+                                 ctypes.POINTER(ctypes.c_int32), i64]
+    lib.pk_tile_walk.restype = i64
+    lib.pk_chunk_arrivals.argtypes = [i64, i64, i32, i32, i32, i32]
+    lib.pk_chunk_arrivals.restype = i64
+    lib.pk_strerror.argtypes = [i32]
+    lib.pk_strerror.restype = ctypes.c_char_p
+    lib.pk_version.argtypes = []
+    lib.pk_version.restype = i32
+    del u32p
+    _lib = lib
+    return lib
+
+
+def pk_strerror(code: int) -> str:
+    return load().pk_strerror(int(code)).decode()
+
+
+def _check(code: int) -> int:
+    if code < 0:
+        raise PkError(code, pk_strerror(code))
+    return code
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _opts(config=0, max_workgroups=0, group_n=0, gemm_only=False):
+    return _Options(int(config), int(max_workgroups), int(group_n), 1 if gemm_only else 0)
+
+
+def _check_tensors(A, B, peer_partials, send_bufs, out, flags):
+    import torch
+    for name, t in (("A", A), ("B", B), ("peer_partials", peer_partials),
+                    ("send_bufs", send_bufs), ("out", out), ("flags", flags)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("A", A), ("B", B), ("peer_partials", peer_partials), ("send_bufs", send_bufs)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    if flags is not None and flags.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("flags must be a 32-bit integer tensor")
+
+
+def pk_gemm_rs_local(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
+                     chunk_rows, tile_order, stream=None) -> int:
+    """Fused share with a float32 ``out``; asynchronous on ``stream``."""
+    _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+    return _check(load().pk_gemm_rs_local(
+        _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
+        int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
+        _stream(stream)))
+
+
+def pk_gemm_rs_local_bf16out(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
+                             chunk_rows, tile_order, stream=None) -> int:
+    """Fused share with a bf16 ``out``; asynchronous on ``stream``."""
+    _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+    return _check(load().pk_gemm_rs_local_bf16out(
+        _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
+        int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
+        _stream(stream)))
+
+
+def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
+                        chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0,
+                        group_n=0, gemm_only=False, stream=None) -> int:
+    """Fused share with explicit tile configuration / grid / grouping options."""
+    _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+    o = _opts(config, max_workgroups, group_n, gemm_only)
+    return _check(load().pk_gemm_rs_local_ex(
+        _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
+        int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
+        int(out_bf16), ctypes.byref(o), _stream(stream)))
+
+
+def pk_flags_words(P, M, chunk_rows) -> int:
+    return _check(load().pk_flags_words(int(P), int(M), int(chunk_rows)))
+
+
+def pk_validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
+                tile_order, out_bf16=0, config=0, max_workgroups=0, group_n=0,
+                gemm_only=False) -> int:
+    """Return code the library would give these arguments (no HIP call).
+
+    Pointer arguments are plain integers (addresses) or None."""
+    o = _opts(config, max_workgroups, group_n, gemm_only)
+    v = [None if p is None else ctypes.c_void_p(int(p)) for p in
+         (A, B, peer_partials, send_bufs, out, flags)]
+    return load().pk_validate(*v, int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),
+                              int(tile_order), int(out_bf16), ctypes.byref(o))
+
+
+def pk_config_count() -> int:
+    return load().pk_config_count()
+
+
+def pk_config_info(cfg_id: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(6)]
+    _check(load().pk_config_info(int(cfg_id), *[ctypes.byref(v) for v in vals]))
+    return dict(zip(("BM", "BN", "BK", "WM", "WN", "threads"), (v.value for v in vals)))
+
+
+def pk_select_config(M, N, K, P) -> int:
+    return _check(load().pk_select_config(int(M), int(N), int(K), int(P)))
+
+
+def pk_tile_walk(M, N, P, rank, config, tile_order, group_n=0) -> np.ndarray:
+    """The tile walk as an int32 array [total, 3] of (shard, row tile, column tile)."""
+    lib = load()
+    total = _check(lib.pk_tile_walk(int(M), int(N), int(P), int(rank), int(config),
+                                    int(tile_order), int(group_n), None, 0))
+    buf = np.zeros((max(total, 1), 3), dtype=np.int32)
+    _check(lib.pk_tile_walk(int(M), int(N), int(P), int(rank), int(config), int(tile_order),
+                            int(group_n), buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            int(total)))
+    return buf[:total]
+
+
+def pk_chunk_arrivals(M, N, P, chunk_rows, config, c) -> int:
+    return _check(load().pk_chunk_arrivals(int(M), int(N), int(P), int(chunk_rows),
+                                           int(config), int(c)))
+
+
+def pk_version() -> int:
+    return load().pk_version()

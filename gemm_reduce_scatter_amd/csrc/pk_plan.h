@@ -1,0 +1,108 @@
+// Tile walk and chunk bookkeeping for the fused GEMM + reduce-scatter share.
+//
+// Shared by the device kernel and the host-side validator/planner (plain
+// inline C++, no HIP types).  The output M x N is split into P row shards of
+// S = M / P rows; every shard is tiled on its own, so a tile never straddles
+// two shards and every shard has the same tile grid:
+//
+//   Tm = ceil(S / BM) row tiles,  Tn = ceil(N / BN) column tiles,
+//   tile (d, t, u) covers shard-local rows [t*BM, min((t+1)*BM, S)) of
+//   shard d and columns [u*BN, min((u+1)*BN, N)).
+//
+// Chunks follow Syncopate section 5.1 ("Communication Schedule
+// Abstraction"): a chunk is a logical block of one or more tiles moved as one
+// unit; here chunk c of a destination is shard-local rows
+// [c*chunk_rows, (c+1)*chunk_rows) at full width.  A chunk's ready word is
+// raised by the last tile that writes into it, so the number of arrivals a
+// chunk waits for is (row tiles overlapping it) x Tn.
+//
+// Tile orders (the order tiles are handed out; results never depend on it,
+// Syncopate section 5.2 "Tile-Scheduler Swizzling" reorders waves the same
+// way without moving data):
+//   0 row-major:        shards 0 .. P-1, each shard chunk-major;
+//   1 owned-first:      shards rank, rank+1, ..., rank+P-1 (mod P);
+//   2 dest-round-robin: position s takes tile s/P of shard (rank+1+s) mod P,
+//                       so consecutive tiles go to different destinations and
+//                       the owned shard comes last in every round.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define PK_HD __host__ __device__ __forceinline__
+#else
+#define PK_HD inline
+#endif
+
+namespace pk {
+
+enum TileOrder : int { kRowMajor = 0, kOwnedFirst = 1, kDestRoundRobin = 2 };
+
+struct TileCoord {
+  int shard;   // owning rank of the tile's rows
+  int t;       // shard-local row-tile index
+  int u;       // column-tile index
+};
+
+struct Grid {
+  int P, rank, S, N, BM, BN, Tm, Tn, order, group_n;
+  PK_HD long long tiles_per_shard() const { return (long long)Tm * Tn; }
+  PK_HD long long total() const { return tiles_per_shard() * P; }
+};
+
+PK_HD int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Position i (0 <= i < Tm*Tn) of the walk inside one shard.  Column tiles are
+// visited in groups of `group_n`: inside a group, all row tiles of a group of
+// columns before the next group.  group_n == Tn gives plain row-major
+// (chunk-major) order; smaller groups keep the A and B panels that run side
+// by side small enough to stay in cache.
+PK_HD void intra_shard(const Grid& g, long long i, int& t, int& u) {
+  const int gn = g.group_n <= 0 || g.group_n > g.Tn ? g.Tn : g.group_n;
+  const long long per_group = (long long)g.Tm * gn;
+  const long long grp = i / per_group;
+  const long long r = i - grp * per_group;
+  const int u0 = (int)grp * gn;
+  const int width = (g.Tn - u0) < gn ? (g.Tn - u0) : gn;   // last group may be narrow
+  t = (int)(r / width);
+  u = u0 + (int)(r - (long long)t * width);
+}
+
+PK_HD TileCoord tile_at(const Grid& g, long long s) {
+  TileCoord c;
+  const long long per = g.tiles_per_shard();
+  long long i;
+  if (g.order == kDestRoundRobin) {
+    c.shard = (int)((g.rank + 1 + s % g.P) % g.P);
+    i = s / g.P;
+  } else if (g.order == kOwnedFirst) {
+    c.shard = (int)((g.rank + s / per) % g.P);
+    i = s % per;
+  } else {
+    c.shard = (int)(s / per);
+    i = s % per;
+  }
+  intra_shard(g, i, c.t, c.u);
+  return c;
+}
+
+// Send slot of destination d (d != rank): ranks in ascending order, skipping
+// the caller.
+PK_HD int slot_of(int d, int rank) { return d < rank ? d : d - 1; }
+
+// Chunks [c_first, c_last] touched by shard-local row tile t.
+PK_HD void chunks_of_row_tile(int t, int BM, int S, int chunk_rows, int& c_first, int& c_last) {
+  const long long r0 = (long long)t * BM;
+  long long r1 = r0 + BM;
+  if (r1 > S) r1 = S;
+  c_first = (int)(r0 / chunk_rows);
+  c_last = (int)((r1 - 1) / chunk_rows);
+}
+
+// Number of tile arrivals chunk c waits for.
+PK_HD unsigned expected_arrivals(int c, int BM, int chunk_rows, int Tn) {
+  const long long r0 = (long long)c * chunk_rows;
+  const long long r1 = r0 + chunk_rows - 1;
+  return (unsigned)((r1 / BM - r0 / BM + 1) * (long long)Tn);
+}
+
+}  // namespace pk

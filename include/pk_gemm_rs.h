@@ -1,0 +1,144 @@
+/*
+ * pk_gemm_rs.h -- C ABI of libpk_gemm_rs.so: one GPU's share of a tile-fused
+ * bf16 GEMM + reduce-scatter on MI355X (gfx950).
+ *
+ * The operation ("ParallelKittens: Systematic and Practical Simplification of
+ * Multi-GPU AI Kernels", section 3 "Scheduling Analysis", the fused GEMM +
+ * reduce-scatter example; "ParallelKittens: Three Principles and Eight
+ * Primitives for Multi-GPU Kernels", section 3 "Principle 2"): P tensor-
+ * parallel ranks each hold A_p (M x K) and B_p (K x N); the result is
+ * C = sum_p A_p * B_p and rank r keeps row shard r, rows [r*S, (r+1)*S) with
+ * S = M / P.  This library runs rank `rank`'s part on one GPU:
+ *
+ *   C_loc = A * B                      bf16 inputs, fp32 accumulation (MFMA)
+ *   for every other rank d: send slot j(d) <- bf16(C_loc rows of shard d)
+ *       and, per chunk of `chunk_rows` rows, a ready word set to 1 once every
+ *       tile of the chunk is stored (the pages' signal primitive; chunks as
+ *       in "Syncopate: Efficient Multi-GPU AI Kernels via Automatic Chunk-
+ *       Centric Compute-Communication Overlap", section 5.1);
+ *   out <- C_loc rows of shard `rank` + sum_j peer_partials[j]   (fp32 adds,
+ *       j ascending), stored once.
+ *
+ * The peers' partials are already staged in device memory (what the other
+ * ranks sent to this one); nothing here talks to another GPU.
+ *
+ * Conventions for every entry point below:
+ *  - All matrices are dense row-major with no padding.  A: bf16 [M][K];
+ *    B: bf16 [K][N]; peer_partials and send_bufs: bf16 [P-1][S][N]; out:
+ *    fp32 or bf16 [S][N].  Slot j of peer_partials / send_bufs belongs to rank
+ *    j if j < rank, else rank j+1 (ascending ranks, skipping `rank`).
+ *  - flags: uint32 [pk_flags_words(P, M, chunk_rows)]: first (P-1)*C ready
+ *    words (slot-major, C = S / chunk_rows chunks per slot), then (P-1)*C
+ *    arrival counters.  All words must be zero at launch.  When the stream
+ *    reaches the end of the call every ready word is 1 and every counter is 0
+ *    again, whatever the tile configuration or tile order.
+ *  - Pointers are device pointers owned by the caller, 16-byte aligned; the
+ *    output buffers (send_bufs, out, flags) must not overlap each other or
+ *    the inputs.  Unused pointers may be NULL: peer_partials, send_bufs and
+ *    flags when P == 1, everything when M == 0 or N == 0.
+ *  - Shapes: M % P == 0, N % 8 == 0, K % 8 == 0 (16-byte rows), chunk_rows
+ *    divides S, 1 <= P <= 64, 0 <= rank < P.  Ragged tiles are handled.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Calls are
+ *    asynchronous: they return after the launch; no host synchronisation,
+ *    no device allocation.  Arguments are validated before any HIP call.
+ *  - Return value: PK_OK or a negative PK_ERR_* code; no exception crosses
+ *    the ABI.  pk_strerror() names the code.
+ *  - Two calls that overlap in time must not share output buffers or flags.
+ */
+#ifndef PK_GEMM_RS_H
+#define PK_GEMM_RS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PK_OK 0
+#define PK_ERR_POINTER (-1)     /* required pointer NULL or not 16-byte aligned */
+#define PK_ERR_SHAPE (-2)       /* M % P, N % 8, K % 8, chunk_rows, negative sizes */
+#define PK_ERR_RANK (-3)        /* P < 1, P > 64, rank outside [0, P) */
+#define PK_ERR_TILE_ORDER (-4)  /* tile_order not 0, 1 or 2 */
+#define PK_ERR_CONFIG (-5)      /* requested tile configuration does not exist */
+#define PK_ERR_LAUNCH (-6)      /* the HIP runtime refused the launch */
+#define PK_ERR_TOO_LARGE (-7)   /* a buffer exceeds the 32-bit element offsets used */
+
+#define PK_TILE_ROW_MAJOR 0       /* shards 0..P-1 in order, chunk-major inside */
+#define PK_TILE_OWNED_FIRST 1     /* owned shard, then rank+1, rank+2, ... (mod P) */
+#define PK_TILE_DEST_ROUND_ROBIN 2 /* one tile per destination in turn, owned last */
+
+/* The fused share with an fp32 `out` (fp32 [S][N]).  See the conventions
+ * above.  tile_order: PK_TILE_*; it changes the order work is done in, never
+ * a bit of any output. */
+int pk_gemm_rs_local(const void* A, const void* B, const void* peer_partials,
+                     void* send_bufs, void* out, uint32_t* flags,
+                     int64_t M, int64_t N, int64_t K, int P, int rank,
+                     int chunk_rows, int tile_order, void* stream);
+
+/* Same as pk_gemm_rs_local with a bf16 `out` (bf16 [S][N], the fp32 sum
+ * rounded to nearest even once). */
+int pk_gemm_rs_local_bf16out(const void* A, const void* B, const void* peer_partials,
+                             void* send_bufs, void* out, uint32_t* flags,
+                             int64_t M, int64_t N, int64_t K, int P, int rank,
+                             int chunk_rows, int tile_order, void* stream);
+
+/* Tuning knobs for pk_gemm_rs_local_ex.  Zero in any field means "library
+ * default".  Schedule knobs follow Syncopate section 5.3 (chunk size, tile
+ * configuration and tile order are searched by measurement). */
+typedef struct pk_options {
+  int config;           /* tile configuration id (pk_config_info), 0 = auto */
+  int max_workgroups;   /* cap on the persistent grid, 0 = fill the device */
+  int group_n;          /* column tiles per locality group inside a shard, 0 = auto */
+  int gemm_only;        /* 1: store bf16(A*B) for all M rows into `out` (bf16 [M][N]);
+                           no send, peers or flags.  The standalone-GEMM reference
+                           the fused kernel is measured against. */
+} pk_options;
+
+/* The fused share with explicit options; out_bf16 selects bf16 (1) or fp32 (0)
+ * `out`.  With opts->gemm_only the call is a plain GEMM (see pk_options). */
+int pk_gemm_rs_local_ex(const void* A, const void* B, const void* peer_partials,
+                        void* send_bufs, void* out, uint32_t* flags,
+                        int64_t M, int64_t N, int64_t K, int P, int rank,
+                        int chunk_rows, int tile_order, int out_bf16,
+                        const pk_options* opts, void* stream);
+
+/* Number of uint32 flag words for (P, M, chunk_rows): 2*(P-1)*(M/P)/chunk_rows,
+ * or a negative PK_ERR_* code for invalid arguments. */
+int64_t pk_flags_words(int P, int64_t M, int chunk_rows);
+
+/* Argument check of pk_gemm_rs_local_ex without any HIP call (host only). */
+int pk_validate(const void* A, const void* B, const void* peer_partials,
+                const void* send_bufs, const void* out, const uint32_t* flags,
+                int64_t M, int64_t N, int64_t K, int P, int rank,
+                int chunk_rows, int tile_order, int out_bf16, const pk_options* opts);
+
+/* Static description of tile configuration `id` (1..pk_config_count()):
+ * block tile BM x BN x BK, wave tile WM x WN, threads per workgroup.
+ * Returns PK_OK or PK_ERR_CONFIG. */
+int pk_config_count(void);
+int pk_config_info(int id, int* BM, int* BN, int* BK, int* WM, int* WN, int* threads);
+
+/* Configuration id the library picks for a shape when opts->config == 0. */
+int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
+
+/* Host copy of the tile walk (host only): writes, for each of the first
+ * min(cap, total) positions, the triple (shard, row tile, column tile) into
+ * out3[3*i .. 3*i+2].  Returns the total number of tiles or a negative code.
+ * group_n as in pk_options (0 = auto for this config). */
+int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,
+                     int group_n, int32_t* out3, int64_t cap);
+
+/* Arrival count chunk c of every slot waits for, under configuration `config`. */
+int64_t pk_chunk_arrivals(int64_t M, int64_t N, int P, int chunk_rows, int config, int c);
+
+/* Human-readable name of a return code. */
+const char* pk_strerror(int code);
+
+/* Library version, 100*major + minor. */
+int pk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PK_GEMM_RS_H */

@@ -275,7 +275,7 @@ def gemm_rs_elements(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits, P: int,
         acc = val[owned]
         amag = mag[owned]
         for j in range(P - 1):
-            pv = bf16_bits_to_f64(np.asarray(peer_bits[j])[lr, lc])
+            pv = bf16_bits_to_f64(peer_bits[j][lr, lc])
             acc = acc + pv
             amag = amag + np.abs(pv)
         val = val.copy()

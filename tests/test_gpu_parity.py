@@ -1,0 +1,347 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Small and medium shapes compare every element; the 32768-wide workloads
+compare sampled elements (each its own fp64 dot product in the oracle) plus
+every flag word, and check invariance across tile orders and chunk sizes on
+the full buffers.  Integer-valued twins must match bit for bit; real-valued
+inputs must meet: relative Frobenius error <= 1e-3 and every element within
+max(2 bf16 ulp, the float32 accumulation bound) of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.gemm_rs_oracle as orc
+from gemm_reduce_scatter_amd import binding as pk
+from gemm_reduce_scatter_amd import inputs as gen
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _native():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pk.load()          # raises if the HIP library is not built
+    yield
+    torch.cuda.synchronize()
+
+
+def _run_and_check(w, out_dtype, integer, seed=0, order=None, chunk_rows=None, **opts):
+    A, B, peers = gen.make_inputs(w, DEV, seed=seed, integer=integer)
+    share = H.Share(w, out_dtype, chunk_rows=chunk_rows)
+    H.run(share, A, B, peers, tile_order=order, **opts)
+    torch.cuda.synchronize()
+    res = H.oracle_for(w, A, B, peers, chunk_rows=share.chunk_rows)
+    if integer:
+        H.compare_exact(res, share)
+        return None
+    mag = orc.local_partial_abs(gen.bf16_bits(A), gen.bf16_bits(B))
+    return H.compare_real(res, mag, share, n_terms=w.K + w.P)
+
+
+# ---------------------------------------------------------------- small / medium
+
+def test_tiny_real():
+    stats = _run_and_check(gen.WORKLOADS["tiny"], "f32", integer=False)
+    print("tiny", stats)
+
+
+def test_tiny_integer_twin_bit_exact():
+    _run_and_check(gen.WORKLOADS["tiny"], "f32", integer=True)
+
+
+MED = gen.Workload("medium", P=4, rank=1, M=1024, N=512, K=192, chunk_rows=64,
+                   ab_dist="normal_sqrtk", peer_dist="normal", out_dtype="f32")
+
+
+@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("order", [0, 1, 2])
+def test_medium_integer_every_config_and_order(config, order):
+    _run_and_check(MED, "f32", integer=True, order=order, config=config)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_medium_real_every_config(config, out_dtype):
+    _run_and_check(MED, out_dtype, integer=False, config=config)
+
+
+# shards of 200 rows, N = 328, K = 136: ragged row tiles in every shard,
+# a ragged last column tile and a partial last K step for every config.
+RAGGED = gen.Workload("ragged", P=3, rank=2, M=600, N=328, K=136, chunk_rows=40,
+                      ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+
+
+@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("integer", [True, False])
+def test_ragged_tails(config, integer):
+    _run_and_check(RAGGED, "bf16", integer=integer, config=config)
+    _run_and_check(RAGGED.with_(rank=0), "f32", integer=integer, config=config, order=2)
+
+
+@pytest.mark.parametrize("chunk_rows", [8, 40, 200])
+def test_chunk_sizes_ragged(chunk_rows):
+    _run_and_check(RAGGED, "f32", integer=True, chunk_rows=chunk_rows)
+
+
+def test_k_zero_gives_peer_sum():
+    w = gen.Workload("k0", P=4, rank=2, M=256, N=64, K=0, chunk_rows=16,
+                     ab_dist="uniform1", peer_dist="int", out_dtype="f32")
+    A = torch.empty((w.M, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, w.N), dtype=torch.bfloat16, device=DEV)
+    _, _, peers = gen.make_inputs(w.with_(K=8), DEV, seed=4, integer=True)
+    share = H.Share(w, "f32")
+    H.run(share, A, B, peers)
+    torch.cuda.synchronize()
+    send, out, _, flags = H.host(share)
+    expect = orc.bf16_bits_to_f64(gen.bf16_bits(peers)).sum(axis=0)
+    assert np.array_equal(out, expect)
+    assert np.all(send == 0)                       # +0.0 everywhere
+    assert np.array_equal(flags, H.expected_flags(w, w.chunk_rows))
+
+
+def test_p1_is_plain_gemm():
+    w = gen.Workload("p1", P=1, rank=0, M=320, N=192, K=96, chunk_rows=64,
+                     ab_dist="uniform1", peer_dist="int", out_dtype="f32")
+    _run_and_check(w, "f32", integer=True)
+    _run_and_check(w, "bf16", integer=False)
+
+
+def test_empty_m_and_n_are_no_ops():
+    w = gen.Workload("empty", P=2, rank=1, M=0, N=64, K=64, chunk_rows=0,
+                     ab_dist="uniform1", peer_dist="int", out_dtype="f32")
+    z = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    assert pk.pk_gemm_rs_local(z, z, z, z, torch.empty(0, device=DEV), None, 0, 64, 64, 2, 1, 0, 0) == 0
+    assert pk.pk_gemm_rs_local(z, z, z, z, torch.empty(0, device=DEV), None, 64, 0, 64, 2, 1, 32, 0) == 0
+    torch.cuda.synchronize()
+    del w
+
+
+def test_invalid_arguments_raise_before_launch():
+    w = gen.WORKLOADS["tiny"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=0)
+    share = H.Share(w, "f32")
+    with pytest.raises(pk.PkError):
+        pk.pk_gemm_rs_local(A, B, peers, share.send, share.out, share.flags,
+                            w.M, w.N, w.K, w.P, 5, w.chunk_rows, 0)
+    with pytest.raises(pk.PkError):
+        pk.pk_gemm_rs_local(A, B, peers, share.send, share.out, share.flags,
+                            w.M, w.N, w.K, w.P, 0, 48, 0)
+    torch.cuda.synchronize()
+    assert share.canaries_intact()
+    assert torch.all(share.flags == 0)             # nothing ran
+
+
+@pytest.mark.parametrize("kind", ["row_lo", "row_hi", "col"])
+def test_placement_probes(kind):
+    w = gen.Workload("probe", P=8, rank=5, M=8192, N=520, K=16, chunk_rows=128,
+                     ab_dist="int", peer_dist="int", out_dtype="f32")
+    A, B, peers = gen.make_probe_inputs(w, kind, DEV)
+    share = H.Share(w, "bf16")
+    H.run(share, A, B, peers, tile_order=2)
+    torch.cuda.synchronize()
+    res = H.oracle_for(w, A, B, peers)
+    H.compare_exact(res, share)
+
+
+def test_gemm_only_mode():
+    w = gen.Workload("gemm", P=8, rank=0, M=1024, N=768, K=256, chunk_rows=128,
+                     ab_dist="int", peer_dist="int", out_dtype="bf16")
+    A, B, _ = gen.make_inputs(w, DEV, seed=9, integer=True)
+    out = torch.full((w.M, w.N), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pk.pk_gemm_rs_local_ex(A, B, None, None, out, None, w.M, w.N, w.K, w.P, 0, 0, 0, 1,
+                           gemm_only=True)
+    torch.cuda.synchronize()
+    C = orc.local_partial(gen.bf16_bits(A), gen.bf16_bits(B))
+    assert np.array_equal(gen.bf16_bits(out), orc.f64_to_bf16_bits(C))
+
+
+# ---------------------------------------------------------------- comm-dominant, full size
+
+CD = gen.WORKLOADS["comm_dominant"]
+
+
+def test_comm_dominant_real_full():
+    stats = _run_and_check(CD, "f32", integer=False)
+    print("comm_dominant", stats)
+
+
+def test_comm_dominant_integer_full():
+    _run_and_check(CD, "f32", integer=True, order=1)
+
+
+def test_outputs_invariant_across_orders_chunks_and_runs():
+    A, B, peers = gen.make_inputs(CD, DEV, seed=5)
+    ref = None
+    for chunk in (64, 128, 256, 512):
+        for order in (0, 1, 2):
+            for grid in (0, 37):
+                share = H.Share(CD, "f32", chunk_rows=chunk)
+                H.run(share, A, B, peers, tile_order=order, max_workgroups=grid)
+                torch.cuda.synchronize()
+                assert torch.equal(share.flags.cpu(), torch.from_numpy(
+                    H.expected_flags(CD, chunk).view(np.int32)))
+                cur = (share.send.view(torch.int16).clone(), share.out.clone())
+                if ref is None:
+                    ref = cur
+                else:
+                    assert torch.equal(cur[0], ref[0]), (chunk, order, grid)
+                    assert torch.equal(cur[1].view(torch.int32), ref[1].view(torch.int32))
+    # a repeat call on the same buffers after re-zeroing the flags
+    share = H.Share(CD, "f32")
+    for _ in range(3):
+        share.reset_flags()
+        H.run(share, A, B, peers)
+    torch.cuda.synchronize()
+    assert torch.equal(share.send.view(torch.int16), ref[0])
+
+
+def test_virtual_ranks_reduce_scatter_on_one_gpu():
+    """All P ranks on one GPU: each rank's send slots feed the others' peers.
+
+    The concatenated shards must equal the sum over ranks of their partials
+    (each sent partial rounded to bf16 once), which for integer inputs is the
+    exact stacked GEMM [A_1..A_P][B_1;..;B_P]."""
+    P = 4
+    w = gen.Workload("vr", P=P, rank=0, M=1024, N=384, K=128, chunk_rows=64,
+                     ab_dist="int", peer_dist="int", out_dtype="f32")
+    As, Bs = [], []
+    for q in range(P):
+        A, B, _ = gen.make_inputs(w, DEV, seed=100 + 10 * q, integer=True)
+        As.append(A)
+        Bs.append(B)
+    zero = torch.zeros((P - 1, w.S, w.N), dtype=torch.bfloat16, device=DEV)
+    sends = []
+    for q in range(P):
+        sh = H.Share(w.with_(rank=q), "f32")
+        H.run(sh, As[q], Bs[q], zero, tile_order=q % 3)
+        sends.append(sh.send.clone())
+    outs = []
+    for r in range(P):
+        peers = torch.stack([sends[q][r if r < q else r - 1] for q in range(P) if q != r])
+        sh = H.Share(w.with_(rank=r), "f32")
+        H.run(sh, As[r], Bs[r], peers.contiguous(), tile_order=(r + 1) % 3)
+        outs.append(sh.out.clone())
+    torch.cuda.synchronize()
+    full = torch.cat(outs).cpu().numpy().astype(np.float64)
+    Acat = np.concatenate([gen.bf16_bits(a) for a in As], axis=1)
+    Bcat = np.concatenate([gen.bf16_bits(b) for b in Bs], axis=0)
+    assert np.array_equal(full, orc.local_partial(Acat, Bcat))
+
+
+# ---------------------------------------------------------------- 32768 workloads, sampled
+
+class _Gathered:
+    """peer_bits[j][lr, lc] for pre-gathered positions (what gemm_rs_elements reads)."""
+
+    def __init__(self, vals):
+        self.vals = vals
+
+    def __getitem__(self, j):
+        v = self.vals[j]
+
+        class _Row:
+            def __getitem__(self, idx):
+                return v
+        return _Row()
+
+
+def _sample_positions(w, n, seed):
+    rng = np.random.default_rng(seed)
+    S = w.S
+    rows = list(rng.integers(0, w.M, n))
+    cols = list(rng.integers(0, w.N, n))
+    # shard, chunk and tile edges
+    for d in range(w.P):
+        for r in (d * S, d * S + 1, d * S + w.chunk_rows - 1, d * S + w.chunk_rows,
+                  (d + 1) * S - 1):
+            for c in (0, 7, 8, 127, 128, 255, 256, w.N - 1):
+                rows.append(r)
+                cols.append(c)
+    return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
+def _check_sampled(w, A, B, peers, share, integer, seed=0, n=3000):
+    rows, cols = _sample_positions(w, n, seed)
+    S = w.S
+    own = (rows // S) == w.rank
+    lr = torch.from_numpy(rows % S).to(DEV)
+    lc = torch.from_numpy(cols).to(DEV)
+    own_t = torch.from_numpy(own).to(DEV)
+    slot = torch.from_numpy(np.where(rows // S < w.rank, rows // S, rows // S - 1)).to(DEV)
+    slot = torch.where(own_t, torch.zeros_like(slot), slot)
+    send_vals = gen.bf16_bits(share.send[slot, lr, lc])
+    if share.out_dtype == "f32":
+        out_vals = share.out[lr, lc].cpu().numpy().astype(np.float64)
+    else:
+        out_vals = orc.bf16_bits_to_f64(gen.bf16_bits(share.out[lr, lc]))
+    pv = gen.bf16_bits(peers[:, lr[own_t], lc[own_t]])
+    kind, val, mag = orc.gemm_rs_elements(gen.bf16_bits(A), gen.bf16_bits(B), _Gathered(pv),
+                                          w.P, w.rank, rows, cols)
+    assert np.array_equal(kind.astype(bool), own)
+    send_ref = orc.f64_to_bf16_bits(val[~own])
+    got_send = send_vals[~own]
+    got_out = out_vals[own]
+    bf16_out = share.out_dtype == "bf16"
+    if integer:
+        assert np.array_equal(got_send, send_ref)
+        ref_out = orc.bf16_bits_to_f64(orc.f64_to_bf16_bits(val[own])) if bf16_out else val[own]
+        assert np.array_equal(got_out, ref_out)
+        return None
+    n_terms = w.K + w.P
+    tol_s = orc.error_bound(mag[~own], n_terms, True, val[~own])
+    es = np.abs(orc.bf16_bits_to_f64(got_send) - val[~own])
+    assert np.all(es <= tol_s), int(np.sum(es > tol_s))
+    tol_o = orc.error_bound(mag[own], n_terms, bf16_out, val[own])
+    eo = np.abs(got_out - val[own])
+    assert np.all(eo <= tol_o), int(np.sum(eo > tol_o))
+    assert orc.rel_frobenius(got_out, val[own]) <= 1e-3
+    return dict(send_exact=float(np.mean(got_send == send_ref)),
+                strict_2ulp_fails=int(np.sum(eo > 2 * orc.ulp_bf16(val[own]))))
+
+
+@pytest.mark.parametrize("name", ["near_threshold", "compute_bound", "large_k"])
+def test_large_workload_sampled(name):
+    w = gen.WORKLOADS[name]
+    print(f"[{name}] generating", flush=True)
+    A, B, peers = gen.make_inputs(w, DEV, seed=0)
+    share = H.Share(w, w.out_dtype)
+    print(f"[{name}] running", flush=True)
+    H.run(share, A, B, peers)
+    torch.cuda.synchronize()
+    assert np.array_equal(share.flags.cpu().numpy().view(np.uint32),
+                          H.expected_flags(w, w.chunk_rows))
+    assert share.canaries_intact()
+    stats = _check_sampled(w, A, B, peers, share, integer=False)
+    print(f"[{name}] real", stats, flush=True)
+    del A, B, peers
+    Ai, Bi, Pi = gen.make_inputs(w, DEV, seed=1, integer=True)
+    share.reset_flags()
+    H.run(share, Ai, Bi, Pi)
+    torch.cuda.synchronize()
+    _check_sampled(w, Ai, Bi, Pi, share, integer=True, seed=1)
+    print(f"[{name}] integer twin exact", flush=True)
+
+
+def test_large_k_sweep_invariance():
+    """The 12 schedule points of the large-K workload give identical bits."""
+    w = gen.WORKLOADS["large_k"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=2)
+    ref = None
+    for chunk in w.sweep_chunk_rows:
+        share = H.Share(w, "bf16", chunk_rows=chunk)
+        for order in (0, 1, 2):
+            share.reset_flags()
+            H.run(share, A, B, peers, tile_order=order)
+            torch.cuda.synchronize()
+            assert np.array_equal(share.flags.cpu().numpy().view(np.uint32),
+                                  H.expected_flags(w, chunk))
+            if ref is None:
+                ref = (share.send.view(torch.int16).clone(), share.out.view(torch.int16).clone())
+            else:
+                assert torch.equal(share.send.view(torch.int16), ref[0]), (chunk, order)
+                assert torch.equal(share.out.view(torch.int16), ref[1]), (chunk, order)
+        del share

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports what the header declares, argument validation, the tile walk and
+the chunk arrival counts."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gemm_reduce_scatter_amd import binding as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pk_gemm_rs.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pk.load()
+    names = _declared_functions()
+    assert "pk_gemm_rs_local" in names and "pk_gemm_rs_local_bf16out" in names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr)
+
+
+def test_version_and_strerror():
+    assert pk.pk_version() >= 100
+    for code in range(-7, 1):
+        assert pk.pk_strerror(code)
+    assert pk.pk_strerror(-99) == "unknown error"
+
+
+def test_flags_words():
+    assert pk.pk_flags_words(8, 4096, 128) == 2 * 7 * 4
+    assert pk.pk_flags_words(8, 32768, 256) == 2 * 7 * 16
+    assert pk.pk_flags_words(2, 256, 64) == 2 * 1 * 2
+    assert pk.pk_flags_words(1, 256, 64) == 0
+    assert pk.pk_flags_words(4, 0, 0) == 0
+    with pytest.raises(pk.PkError):
+        pk.pk_flags_words(3, 256, 64)       # M % P
+    with pytest.raises(pk.PkError):
+        pk.pk_flags_words(2, 256, 48)       # chunk does not divide S
+    with pytest.raises(pk.PkError):
+        pk.pk_flags_words(0, 256, 64)
+
+
+# Fake but aligned addresses: pk_validate never dereferences them.
+GOOD = dict(A=0x10000, B=0x20000, peer_partials=0x30000, send_bufs=0x40000, out=0x50000,
+            flags=0x60000)
+
+
+def _v(**kw):
+    args = dict(GOOD)
+    args.update(dict(M=256, N=256, K=128, P=2, rank=0, chunk_rows=64, tile_order=0))
+    args.update(kw)
+    return pk.pk_validate(args["A"], args["B"], args["peer_partials"], args["send_bufs"],
+                          args["out"], args["flags"], args["M"], args["N"], args["K"], args["P"],
+                          args["rank"], args["chunk_rows"], args["tile_order"],
+                          args.get("out_bf16", 0), args.get("config", 0),
+                          args.get("max_workgroups", 0), args.get("group_n", 0),
+                          args.get("gemm_only", False))
+
+
+def test_validate_accepts_good_arguments():
+    assert _v() == 0
+    assert _v(out_bf16=1) == 0
+    assert _v(P=1, rank=0, peer_partials=None, send_bufs=None, flags=None) == 0
+    assert _v(M=0, A=None, B=None, out=None) == 0
+    assert _v(K=0, A=None, B=None) == 0
+    assert _v(gemm_only=True, peer_partials=None, send_bufs=None, flags=None) == 0
+    for cfg in range(1, pk.pk_config_count() + 1):
+        assert _v(config=cfg) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), -1), (dict(B=0x20008), -1), (dict(out=None), -1), (dict(flags=None), -1),
+    (dict(send_bufs=None), -1), (dict(peer_partials=0x30001), -1), (dict(flags=0x60002), -1),
+    (dict(M=255), -2), (dict(N=12), -2), (dict(K=12), -2), (dict(chunk_rows=48), -2),
+    (dict(chunk_rows=0), -2), (dict(M=-2), -2), (dict(out_bf16=2), -2),
+    (dict(P=0), -3), (dict(rank=2), -3), (dict(rank=-1), -3), (dict(P=65, M=65 * 64), -3),
+    (dict(tile_order=3), -4), (dict(tile_order=-1), -4),
+    (dict(config=99), -5), (dict(max_workgroups=-1), -5),
+])
+def test_validate_rejects(kw, code):
+    assert _v(**kw) == code
+
+
+def test_config_table():
+    n = pk.pk_config_count()
+    assert n >= 3
+    for i in range(1, n + 1):
+        c = pk.pk_config_info(i)
+        assert c["BM"] % c["WM"] == 0 and c["BN"] % c["WN"] == 0
+        assert c["threads"] == 64 * (c["BM"] // c["WM"]) * (c["BN"] // c["WN"])
+    with pytest.raises(pk.PkError):
+        pk.pk_config_info(0)
+
+
+def test_select_config_for_the_workloads():
+    big = pk.pk_config_info(pk.pk_select_config(32768, 32768, 4096, 8))
+    assert big["BM"] == 256 and big["BN"] == 256
+    mid = pk.pk_config_info(pk.pk_select_config(4096, 4096, 512, 8))
+    assert mid["BM"] <= 512 // 4        # at least 4 row tiles per shard
+    tiny = pk.pk_config_info(pk.pk_select_config(256, 256, 128, 2))
+    assert tiny["BM"] <= 128
+
+
+# ---------------------------------------------------------------- tile walk
+
+def _tiles(M, N, P, cfg):
+    c = pk.pk_config_info(cfg)
+    S = M // P
+    Tm = -(-S // c["BM"])
+    Tn = -(-N // c["BN"])
+    return Tm, Tn
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("shape", [(256, 256, 2, 0, 3), (4096, 4096, 8, 3, 2), (600, 200, 3, 1, 3),
+                                   (8192, 1024, 8, 7, 1)])
+@pytest.mark.parametrize("group_n", [0, 1, 3])
+def test_tile_walk_is_a_permutation(order, shape, group_n):
+    M, N, P, rank, cfg = shape
+    Tm, Tn = _tiles(M, N, P, cfg)
+    w = pk.pk_tile_walk(M, N, P, rank, cfg, order, group_n)
+    assert w.shape == (P * Tm * Tn, 3)
+    keys = {tuple(r) for r in w.tolist()}
+    assert keys == {(d, t, u) for d in range(P) for t in range(Tm) for u in range(Tn)}
+
+
+def test_tile_orders_follow_their_definitions():
+    M, N, P, rank, cfg = 4096, 4096, 8, 3, 2
+    Tm, Tn = _tiles(M, N, P, cfg)
+    per = Tm * Tn
+    rm = pk.pk_tile_walk(M, N, P, rank, cfg, 0)
+    assert list(rm[:, 0]) == [d for d in range(P) for _ in range(per)]
+    # inside a shard: chunk-major (row tile outer, column tile inner)
+    assert [tuple(x) for x in rm[:per, 1:]] == [(t, u) for t in range(Tm) for u in range(Tn)]
+    of = pk.pk_tile_walk(M, N, P, rank, cfg, 1)
+    assert list(of[:, 0]) == [(rank + i) % P for i in range(P) for _ in range(per)]
+    rr = pk.pk_tile_walk(M, N, P, rank, cfg, 2)
+    assert list(rr[:P, 0]) == [(rank + 1 + i) % P for i in range(P)]
+    assert rr[P - 1, 0] == rank                    # owned shard last in each round
+    assert all(len(set(rr[i * P:(i + 1) * P, 0])) == P for i in range(per))
+    assert np.array_equal(rr[::P, 1:], rm[:per, 1:])
+
+
+def test_grouped_walk_visits_column_groups():
+    M, N, P, rank, cfg = 8192, 2048, 2, 0, 2    # Tm = 32, Tn = 16
+    Tm, Tn = _tiles(M, N, P, cfg)
+    w = pk.pk_tile_walk(M, N, P, rank, cfg, 0, group_n=4)
+    first = w[:Tm * 4]
+    assert set(first[:, 2]) == {0, 1, 2, 3} and set(first[:, 1]) == set(range(Tm))
+
+
+# ---------------------------------------------------------------- chunk arrivals
+
+@pytest.mark.parametrize("M,N,P,chunk,cfg", [(4096, 4096, 8, 128, 2), (256, 256, 2, 64, 3),
+                                             (32768, 32768, 8, 1024, 1), (600, 200, 3, 8, 3),
+                                             (600, 200, 3, 200, 2), (2400, 520, 3, 40, 1)])
+def test_chunk_arrivals_count_overlapping_tiles(M, N, P, chunk, cfg):
+    c = pk.pk_config_info(cfg)
+    S = M // P
+    Tm, Tn = _tiles(M, N, P, cfg)
+    for ci in range(S // chunk):
+        lo, hi = ci * chunk, (ci + 1) * chunk       # shard-local rows
+        n = sum(1 for t in range(Tm)
+                if max(lo, t * c["BM"]) < min(hi, min((t + 1) * c["BM"], S))) * Tn
+        assert pk.pk_chunk_arrivals(M, N, P, chunk, cfg, ci) == n
