@@ -108,7 +108,10 @@ def compare_real(res: orc.OracleResult, mag_C, share: Share, n_terms: int):
     assert np.all(np.isfinite(out)), "non-finite output"
     bad = err > tol
     assert not np.any(bad), f"{int(bad.sum())} owned elements out of tolerance, max err {err.max()}"
-    rel = orc.rel_frobenius(out, res.out)
+    # A bf16 shard is compared with the oracle's shard rounded once to bf16:
+    # bf16 rounding alone is ~1.3e-3 relative (RMS), above the 1e-3 budget.
+    ref_frob = orc.bf16_bits_to_f64(res.out_bf16_bits()) if bf16_out else res.out
+    rel = orc.rel_frobenius(out, ref_frob)
     assert rel <= 1e-3, rel
     strict = int(np.sum(err > 2.0 * orc.ulp_bf16(res.out)))
     # send buffers: bf16 of the fp32 accumulation vs the exact value

@@ -298,7 +298,8 @@ def _check_sampled(w, A, B, peers, share, integer, seed=0, n=3000):
     tol_o = orc.error_bound(mag[own], n_terms, bf16_out, val[own])
     eo = np.abs(got_out - val[own])
     assert np.all(eo <= tol_o), int(np.sum(eo > tol_o))
-    assert orc.rel_frobenius(got_out, val[own]) <= 1e-3
+    ref_frob = orc.bf16_bits_to_f64(orc.f64_to_bf16_bits(val[own])) if bf16_out else val[own]
+    assert orc.rel_frobenius(got_out, ref_frob) <= 1e-3
     return dict(send_exact=float(np.mean(got_send == send_ref)),
                 strict_2ulp_fails=int(np.sum(eo > 2 * orc.ulp_bf16(val[own]))))
 
