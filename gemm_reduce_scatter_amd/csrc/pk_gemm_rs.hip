@@ -12,8 +12,14 @@
 //  * tiles for other ranks go to per-destination chunked send buffers, and
 //    the last tile of a chunk raises its ready word (chunks as in Syncopate,
 //    section 5.1);
+//  * operand tiles move global -> LDS by buffer loads that write LDS
+//    directly (no register staging); lanes outside the matrix read zero
+//    through the buffer range check, which also covers ragged tiles and a
+//    partial last K step;
 //  * the main loop is bf16 MFMA (v_mfma_f32_32x32x16_bf16) on 64-wide
-//    wavefronts fed from LDS, double buffered;
+//    wavefronts.  A is read from LDS with 16-byte reads; B stays n-major in
+//    LDS as it is in memory and is read with the CDNA4 transposing LDS read
+//    (ds_read_b64_tr_b16), which hands each lane the k-run of one column;
 //  * one persistent workgroup per CU slot walks the tile order; consecutive
 //    walk positions go to the same XCD so tiles that share A/B panels share
 //    that XCD's L2.
@@ -29,39 +35,67 @@ namespace pk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define PK_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------------------
-// Tile configurations.
+// Tile configurations.  Four waves (256 threads) per workgroup in a
+// WAVES_M x WAVES_N arrangement; each wave owns a WM x WN block of 32x32
+// MFMA accumulators.  STAGES-deep ring of LDS operand buffers of BK k each.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = WAVES * 64;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 MFMA blocks per wave
-  static constexpr int KCH = BK / 8;                 // 16-byte chunks per LDS row
-  static constexpr int A_CHUNKS = BM * KCH;          // per stage
-  static constexpr int B_CHUNKS = BN * KCH;
-  static constexpr int A_PER_THREAD = A_CHUNKS / THREADS;
-  static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);       // 8x8 element blocks
-  static constexpr int B_PER_THREAD = (B_BLOCKS + THREADS - 1) / THREADS;
-  static constexpr int STAGE_CHUNKS = A_CHUNKS + B_CHUNKS;
-  static constexpr int LDS_MAIN = 2 * STAGE_CHUNKS * 16;     // bytes
-  static constexpr int EPI_STRIDE = WN + 8;                  // floats per staged row
-  static constexpr int LDS_EPI = WAVES * 32 * EPI_STRIDE * 4;
-  static constexpr int LDS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
-  static_assert(A_CHUNKS % THREADS == 0, "A tile must split evenly over threads");
+  static constexpr int KK = BK / 16;                 // k16 MFMA steps per stage
+  // LDS operand layout, per stage:
+  //   A: BM rows of BK k (A_CPR chunks of 16 bytes), chunk c of row r stored
+  //      at chunk c ^ swz_a(r);
+  //   B: BK k-rows of BN n (B_CPR chunks), chunk c of k-row k stored at
+  //      chunk c ^ swz_b(k).
+  static constexpr int A_CPR = BK / 8;
+  static constexpr int A_RPL = 64 / A_CPR;            // A rows per 64-lane load
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * 2;
+  static constexpr int B_CPR = BN / 8;                // 16-byte chunks per B row
+  static constexpr int B_RPL = 64 / B_CPR;            // B rows per 64-lane load
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;   // 1 KiB per wave load
+  static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+  static constexpr int LOADS = A_LOADS + B_LOADS;          // per wave per stage
+  static constexpr int EPI_STRIDE = WN + 8;                // floats per staged row
+  static constexpr int LDS_EPI = WAVES * 16 * EPI_STRIDE * 4;  // 16-row half stripes
+  // Stage buffers are separate LDS arrays (the compiler then knows that reads
+  // of one stage never alias the DMA into another); the epilogue staging
+  // area reuses stage 0.
+  static constexpr int LDS0 = STAGE_BYTES > LDS_EPI ? STAGE_BYTES : LDS_EPI;
+  static constexpr int LDS = LDS0 + (STAGES - 1) * STAGE_BYTES;
+  static_assert(WAVES == 4, "four waves per workgroup");
+  static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
+  static_assert(A_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0, "A stage splits over the waves");
+  static_assert(B_LOADS >= 1 && B_BYTES % (1024 * WAVES) == 0, "B stage splits over the waves");
+  static_assert(B_CPR >= 8 && B_CPR <= 64, "B row is 8..64 chunks");
+  static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a CU");
+  static_assert(LOADS % KK == 0, "loads split over the k16 steps");
 };
 
-// id 1..3; the table in pk_config_info mirrors these.
-using Cfg1 = Cfg<256, 256, 128, 128>;
-using Cfg2 = Cfg<128, 128, 64, 64>;
-using Cfg3 = Cfg<64, 64, 32, 32>;
+// id 1..5; the table in pk_config_info mirrors these.
+using Cfg1 = Cfg<256, 256, 2, 2, 32, 4>;
+using Cfg2 = Cfg<128, 128, 2, 2, 64, 2>;
+using Cfg3 = Cfg<64, 64, 2, 2, 64, 2>;
+using Cfg4 = Cfg<256, 128, 2, 2, 32, 4>;
+using Cfg5 = Cfg<256, 256, 2, 2, 64, 2>;
 
 struct KArgs {
   const uint16_t* A;
@@ -70,16 +104,45 @@ struct KArgs {
   uint16_t* send;
   void* out;
   uint32_t* flags;
-  long long M, N, K;
+  long long M;
+  int N, K;            // N <= 2^24, K <= 2^22 (validated)
   int P, rank, S, chunk_rows, n_chunks;
-  int out_bf16, gemm_only;
+  int out_bf16;
   Grid g;
   long long total_tiles;
 };
 
-// LDS swizzle: 16-byte chunk c of row r lives at chunk c ^ swz(r), so 16
-// consecutive rows read at one logical chunk hit 16 distinct bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// LDS swizzles.  A: the 16 rows a 16-lane group reads at one logical chunk
+// land in 16 distinct 16-byte bank groups, and so do the 8 rows of each
+// 8-lane quarter; the swizzle depends on r % 16 only, so it is the same for
+// every 32-row fragment and every load of a lane.  B: the four k-rows a
+// transposing read touches (k % 4 = 0..3) land in distinct bank groups for
+// both the 16- and the 32-lane halves of the read.
+template <int BK>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (BK == 64) return (r ^ ((r >> 3) & 1)) & 7;   // 128-byte rows
+  else return ((r >> 1) ^ (r >> 3)) & 3;                     // 64-byte rows
+}
+template <int CPR>
+__device__ __forceinline__ int swz_b(int k) {
+  const int j = k & 3;
+  return (((j & 1) << 2) + (j >> 1) * 10) & (CPR - 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  // Range 2^31 bytes: offsets of lanes outside the matrix are set to 2^31 and
+  // read as zero.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0x80000000,
+                                           0x00020000);
+}
+constexpr uint32_t kOffNone = 0x80000000u;
+
+// 16 bytes per lane from r + voff + soff into LDS at dst + 16 * lane.  soff is
+// wave-uniform; voff of a lane outside the matrix is kOffNone.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, PK_LDS void* dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)voff, (int)soff, 0, 0);
+}
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -95,145 +158,202 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// s_waitcnt with vmcnt = N (0..63) and the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wave-local ordering of LDS writes before LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
-// One output tile: main loop + fused epilogue.
+// Operand staging: one stage (BK k) of the A row panel and the B column
+// panel of a tile, global -> LDS.
 // ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void load_a(const KArgs& a, const TileCoord& tc, int k0, int tid,
-                                       u32x4 (&ra)[C::A_PER_THREAD]) {
-#pragma unroll
-  for (int i = 0; i < C::A_PER_THREAD; ++i) {
-    const int idx = tid + i * C::THREADS;
-    const int r = idx / C::KCH, c = idx % C::KCH;
-    const int lr = tc.t * C::BM + r;               // shard-local row
-    const int k = k0 + c * 8;
-    const bool ok = (lr < a.S) && (k < a.K);
-    const uint16_t* p = a.A + ((long long)tc.shard * a.S + lr) * a.K + k;
-    ra[i] = ok ? load16(p) : u32x4{0u, 0u, 0u, 0u};
-  }
-}
+struct Loader {
+  // per-lane constants
+  uint32_t a_off;      // byte offset of this lane's A chunk for load 0 at k0 = 0
+  int a_row;           // row of load 0 relative to the tile
+  int a_kc;            // k offset (elements) of this lane's A chunk
+  uint32_t b_off;      // byte offset of this lane's B chunk for load 0 at k0 = 0
+  int b_k;             // k-row of load 0
+  int b_nc;            // n offset (elements) of this lane's B chunk
 
-template <class C>
-__device__ __forceinline__ void load_b(const KArgs& a, const TileCoord& tc, int k0, int tid,
-                                       u32x4 (&rb)[C::B_PER_THREAD][8]) {
-#pragma unroll
-  for (int i = 0; i < C::B_PER_THREAD; ++i) {
-    const int b = tid + i * C::THREADS;
-    const int kb = b / (C::BN / 8), nb = b % (C::BN / 8);
-    const long long n = (long long)tc.u * C::BN + nb * 8;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int k = k0 + kb * 8 + r;
-      const bool ok = (b < C::B_BLOCKS) && (k < a.K) && (n < a.N);
-      rb[i][r] = ok ? load16(a.B + (long long)k * a.N + n) : u32x4{0u, 0u, 0u, 0u};
-    }
+  __device__ __forceinline__ void init(const KArgs& a, int wave, int lane) {
+    // A: load q of wave w covers LDS rows (q*WAVES + w)*A_RPL .. +A_RPL-1;
+    // lane i fills row +i/A_CPR, physical chunk i%A_CPR, which holds logical
+    // chunk (i%A_CPR)^swz_a.  swz_a depends on the row mod 16, the same for
+    // every q.
+    a_row = wave * C::A_RPL + lane / C::A_CPR;
+    a_kc = 8 * ((lane % C::A_CPR) ^ swz_a<C::BK>(a_row));
+    a_off = (uint32_t)(a_row * a.K + a_kc) * 2u;
+    // B: load q of wave w covers k-rows (q*WAVES + w)*B_RPL .. +B_RPL-1.
+    b_k = wave * C::B_RPL + lane / C::B_CPR;
+    b_nc = 8 * ((lane % C::B_CPR) ^ swz_b<C::B_CPR>(b_k));
+    b_off = (uint32_t)(b_k * a.N + b_nc) * 2u;
   }
-}
 
-template <class C>
-__device__ __forceinline__ void store_a(u32x4* lds_a, int tid, const u32x4 (&ra)[C::A_PER_THREAD]) {
-#pragma unroll
-  for (int i = 0; i < C::A_PER_THREAD; ++i) {
-    const int idx = tid + i * C::THREADS;
-    const int r = idx / C::KCH, c = idx % C::KCH;
-    lds_a[r * C::KCH + (c ^ swz(r))] = ra[i];
+  // Per-stage descriptors: A rows from row0, B columns from col0, both at k0.
+  struct Stage {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int k0;
+  };
+  __device__ __forceinline__ Stage stage(const KArgs& a, long long row0, int col0,
+                                         int k0) const {
+    Stage st;
+    st.ra = make_rsrc(a.A + row0 * a.K + k0);
+    st.rb = make_rsrc(a.B + (long long)k0 * a.N + col0);
+    st.k0 = k0;
+    return st;
   }
-}
 
-// B arrives as 8 k-rows x 8 n-columns per thread and is stored transposed
-// (n-major, k contiguous) so that each MFMA lane reads its 8 k-values of one
-// column with a single 16-byte LDS read.
-template <class C>
-__device__ __forceinline__ void store_b(u32x4* lds_b, int tid, const u32x4 (&rb)[C::B_PER_THREAD][8]) {
+  // Issue loads [Q0, Q1) of this wave's A loads followed by its B loads
+  // (numbered 0 .. LOADS-1) of one stage into `dst`.  The per-load step is a
+  // scalar offset; lanes outside the matrix (rows past the shard, columns
+  // past N, k past K) get a vector offset past the descriptor range and
+  // load zeros.
+  template <int Q0, int Q1>
+  __device__ __forceinline__ void issue(const KArgs& a, const Stage& st, unsigned char* dst,
+                                        int wave, int rows_valid, int col0) const {
+    const bool a_k_ok = st.k0 + a_kc < a.K;
+    const bool b_n_ok = col0 + b_nc < a.N;
 #pragma unroll
-  for (int i = 0; i < C::B_PER_THREAD; ++i) {
-    const int b = tid + i * C::THREADS;
-    if (b < C::B_BLOCKS) {
-      const int kb = b / (C::BN / 8), nb = b % (C::BN / 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = j >> 1;
-        u32x4 o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = rb[i][2 * p][q], hi = rb[i][2 * p + 1][q];
-          o[p] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        const int n = nb * 8 + j;
-        lds_b[n * C::KCH + (kb ^ swz(n))] = o;
+    for (int q = Q0; q < Q1; ++q) {
+      if (q < C::A_LOADS) {
+        const bool ok = a_k_ok & (a_row + q * C::WAVES * C::A_RPL < rows_valid);
+        const uint32_t soff = (uint32_t)(q * C::WAVES * C::A_RPL) * (uint32_t)a.K * 2u;
+        dma16(st.ra, (PK_LDS void*)(dst + (q * C::WAVES + wave) * 1024), ok ? a_off : kOffNone,
+              soff);
+      } else {
+        const int qb = q - C::A_LOADS;
+        const bool ok = b_n_ok & (st.k0 + b_k + qb * C::WAVES * C::B_RPL < a.K);
+        const uint32_t soff = (uint32_t)(qb * C::WAVES * C::B_RPL) * (uint32_t)a.N * 2u;
+        dma16(st.rb, (PK_LDS void*)(dst + C::A_BYTES + (qb * C::WAVES + wave) * 1024),
+              ok ? b_off : kOffNone, soff);
       }
     }
   }
-}
+};
 
+// ---------------------------------------------------------------------------
+// MFMA over one LDS stage.
+// ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void mma_stage(const u32x4* lds_a, const u32x4* lds_b, int wm, int wn,
-                                          int lane, f32x16 (&acc)[C::FM][C::FN]) {
+struct Reader {
+  uint32_t a_base;            // this lane's A row (fragment 0) byte offset in a stage
+  uint32_t a_x[C::KK];        // swizzled chunk byte offset for k16 step kk
+  uint32_t b_base[C::FN];     // this lane's B address part for fragment fn (row + chunk)
+
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    const int r = wm * C::WM + (lane & 31);
+    a_base = (uint32_t)r * (uint32_t)(C::BK * 2);
+    const int sa = swz_a<C::BK>(r);
 #pragma unroll
-  for (int kk = 0; kk < C::BK / 16; ++kk) {
-    const int ch = kk * 2 + (lane >> 5);
-    bf16x8 af[C::FM], bf[C::FN];
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int r = wm * C::WM + fm * 32 + (lane & 31);
-      af[fm] = __builtin_bit_cast(bf16x8, lds_a[r * C::KCH + (ch ^ swz(r))]);
-    }
+    for (int kk = 0; kk < C::KK; ++kk) a_x[kk] = (uint32_t)(((2 * kk + (lane >> 5)) ^ sa) << 4);
+    // Transposing B read: 16-lane group g reads k-rows kbase + 0..3 (one per
+    // lane quad j) at columns nbase + 4i .. +3 (lane i of the quad); after
+    // the transpose lane t of the group holds rows kbase + 0..3 of column
+    // nbase + t.  MFMA 32x32x16 wants lane L to hold k = 8*(L/32) + 0..7 of
+    // column L%32: group g gets nbase = 16*(g&1), kbase = 8*(g>>1), and a
+    // second read at kbase + 4 gives k + 4..7.
+    const int g = lane >> 4, t = lane & 15, i = t & 3, j = t >> 2;
+    const int krow = 8 * (g >> 1) + j;
+    const int sb = swz_b<C::B_CPR>(krow);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int n = wn * C::WN + fn * 32 + (lane & 31);
-      bf[fn] = __builtin_bit_cast(bf16x8, lds_b[n * C::KCH + (ch ^ swz(n))]);
+      const int n = wn * C::WN + fn * 32 + 16 * (g & 1) + 4 * i;
+      b_base[fn] = (uint32_t)C::A_BYTES + (uint32_t)krow * (uint32_t)(C::BN * 2) +
+                   (uint32_t)((((n >> 3) ^ sb) << 4) + ((n & 4) << 1));
     }
+  }
+
+  struct Frags {
+    bf16x8 a[C::FM], b[C::FN];
+  };
+
+  __device__ __forceinline__ void read(const unsigned char* st, int kk, Frags& f) const {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      f.a[fm] = *reinterpret_cast<const bf16x8*>(st + a_base + fm * 32 * (C::BK * 2) + a_x[kk]);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const unsigned char* p = st + b_base[fn] + kk * 16 * (C::BN * 2);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PK_LDS s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PK_LDS s16x4*)(p + 4 * C::BN * 2));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      f.b[fn] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
+  }
+
+  __device__ __forceinline__ static void mfma(const Frags& f, f32x16 (&acc)[C::FM][C::FN]) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[fm], f.b[fn], acc[fm][fn], 0, 0, 0);
+  }
+};
+
+// One stage of the main loop: MFMA over `cur` (KK k16 steps, fragments of
+// step kk+1 read while step kk multiplies) while a share of the loads of the
+// stage STAGES-1 ahead, into `nxt`, is issued before each step.  A stage past
+// K loads zeros (every lane fails the k bound), so the loop body has no
+// branches, the number of loads in flight is fixed, and the accumulators stay
+// in place across iterations.  The stage ends when this wave's loads of the
+// next stage have landed and every wave has finished reading `cur`.
+template <class C, int KKI>
+__device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
+                                            const typename Loader<C>::Stage& ns,
+                                            const Reader<C>& rd, const unsigned char* cur,
+                                            unsigned char* nxt, int wave, int rows_valid,
+                                            int col0, f32x16 (&acc)[C::FM][C::FN],
+                                            typename Reader<C>::Frags (&f)[2]) {
+  if constexpr (KKI < C::KK) {
+    constexpr int QP = C::LOADS / C::KK;
+    ld.template issue<KKI * QP, (KKI + 1) * QP>(a, ns, nxt, wave, rows_valid, col0);
+    if constexpr (KKI + 1 < C::KK) rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
+    Reader<C>::mfma(f[KKI & 1], acc);
+    stage_steps<C, KKI + 1>(a, ld, ns, rd, cur, nxt, wave, rows_valid, col0, acc, f);
   }
 }
 
-// Epilogue for 8 consecutive columns of one row of the tile.
-__device__ __forceinline__ void emit8(const KArgs& a, const TileCoord& tc, int lr, long long col,
-                                      const float (&v)[8]) {
-  if (a.gemm_only) {
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((long long)tc.shard * a.S + lr) * a.N + col;
-    *reinterpret_cast<u32x4*>(dst) = o;
-    return;
-  }
-  if (tc.shard != a.rank) {
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
-    const int slot = slot_of(tc.shard, a.rank);
-    uint16_t* dst = a.send + ((long long)slot * a.S + lr) * a.N + col;
-    *reinterpret_cast<u32x4*>(dst) = o;
-    return;
-  }
-  float s[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = v[e];
-  const long long base = (long long)lr * a.N + col;
-  const long long slot_stride = (long long)a.S * a.N;
-  for (int j = 0; j < a.P - 1; ++j) {          // ascending slot order
-    const u32x4 pv = load16(a.peers + j * slot_stride + base);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      s[2 * p] += bf16lo(pv[p]);
-      s[2 * p + 1] += bf16hi(pv[p]);
-    }
-  }
-  if (a.out_bf16) {
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(s[2 * p], s[2 * p + 1]);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + base) = o;
-  } else {
-    float* dst = reinterpret_cast<float*>(a.out) + base;
-    *reinterpret_cast<f32x4*>(dst) = f32x4{s[0], s[1], s[2], s[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{s[4], s[5], s[6], s[7]};
-  }
+template <class C>
+__device__ __forceinline__ void main_stage(const KArgs& a, const Loader<C>& ld,
+                                           const typename Loader<C>::Stage& ns,
+                                           const Reader<C>& rd, const unsigned char* cur,
+                                           unsigned char* nxt, int wave, int rows_valid,
+                                           int col0, f32x16 (&acc)[C::FM][C::FN]) {
+  typename Reader<C>::Frags f[2];
+  rd.read(cur, 0, f[0]);
+  stage_steps<C, 0>(a, ld, ns, rd, cur, nxt, wave, rows_valid, col0, acc, f);
+  // This wave's loads of the next stage have landed; every read of `cur` has
+  // returned (its fragments were consumed by the MFMAs above).  A bare
+  // barrier then suffices: a workgroup fence here would also wait for the
+  // loads still in flight for the stages after the next.
+  wait_vm<(C::STAGES - 2) * C::LOADS>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Stage buffer I of the ring (compile-time, so every LDS access names one
+// array).
+template <int I>
+__device__ __forceinline__ unsigned char* pick(unsigned char* b0, unsigned char* b1,
+                                               unsigned char* b2, unsigned char* b3) {
+  if constexpr (I == 0) return b0;
+  else if constexpr (I == 1) return b1;
+  else if constexpr (I == 2) return b2;
+  else return b3;
 }
 
 // Ready-word protocol for one finished send tile.  Every thread has already
@@ -260,15 +380,130 @@ __device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& t
   }
 }
 
-template <class C>
-__global__ void __launch_bounds__(C::THREADS) gemm_rs_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
-  u32x4* lds = reinterpret_cast<u32x4*>(smem);
-  float* lds_f = reinterpret_cast<float*>(smem);
+enum Mode : int { kFused = 0, kGemmOnly = 1 };
+
+// ---------------------------------------------------------------------------
+// Epilogue of one tile.  Each wave re-lays its accumulators, one 16-row half
+// of a 32-row stripe at a time, through LDS so that every lane owns 8
+// consecutive columns of one row (16-byte global accesses), then sends, sums
+// or stores.
+// ---------------------------------------------------------------------------
+template <class C, int MODE, int GS>
+__device__ __forceinline__ void epilogue(const KArgs& a, const TileCoord& tc,
+                                         float* lds_f, int wave, int wm, int wn, int lane,
+                                         f32x16 (&acc)[C::FM][C::FN]) {
+  float* stage = lds_f + wave * 16 * C::EPI_STRIDE;
+  constexpr int LPR = C::WN / 8;                 // lanes per staged row
+  constexpr int RPI = 64 / LPR;                  // rows per pass
+  constexpr int PASSES = 16 / RPI;
+  // owned segments summed together: 4 for small wave tiles, 2 when the
+  // accumulators take a large part of the register file
+  constexpr int BATCH = C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4);
+  static_assert(PASSES % BATCH == 0, "batches tile the passes");
+  const bool owned = MODE == kFused && tc.shard == a.rank;
+  const int c8 = lane % LPR;
+  const long long col = (long long)tc.u * C::BN + wn * C::WN + c8 * 8;
+  const bool col_ok = col < a.N;
+  const long long slot_stride = (long long)a.S * a.N;
+  const int slot = MODE == kFused && !owned ? slot_of(tc.shard, a.rank) : 0;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // accumulator registers 8h .. 8h+7 hold rows 16h .. 16h+15 of the stripe
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - 16 * h;
+          stage[row * C::EPI_STRIDE + fn * 32 + (lane & 31)] = acc[fm][fn][r];
+        }
+      wave_lds_sync();
+      const int lr0 = tc.t * C::BM + wm * C::WM + fm * 32 + 16 * h;   // shard-local row
+      if (!owned) {
+#pragma unroll
+        for (int it = 0; it < PASSES; ++it) {
+          const int rr = it * RPI + lane / LPR;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
+          const int lr = lr0 + rr;
+          if (lr < a.S && col_ok) {
+            const u32x4 o = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                             pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+            uint16_t* dst;
+            if (MODE == kGemmOnly)
+              dst = reinterpret_cast<uint16_t*>(a.out) + ((long long)tc.shard * a.S + lr) * a.N + col;
+            else
+              dst = a.send + (slot * (long long)a.S + lr) * a.N + col;
+            *reinterpret_cast<u32x4*>(dst) = o;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int it0 = 0; it0 < PASSES; it0 += BATCH) {
+          float s[BATCH][8];
+          bool ok[BATCH];
+          long long base[BATCH];
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            const int rr = (it0 + b) * RPI + lane / LPR;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
+            s[b][0] = x0[0]; s[b][1] = x0[1]; s[b][2] = x0[2]; s[b][3] = x0[3];
+            s[b][4] = x1[0]; s[b][5] = x1[1]; s[b][6] = x1[2]; s[b][7] = x1[3];
+            const int lr = lr0 + rr;
+            ok[b] = lr < a.S && col_ok;
+            base[b] = ok[b] ? (long long)lr * a.N + col : 0;   // row 0 stays in bounds
+          }
+          // ascending slot order; GS slots' loads are in flight together
+          for (int j0 = 0; j0 < a.P - 1; j0 += GS) {
+            u32x4 pv[BATCH][GS];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+              for (int jj = 0; jj < GS; ++jj)
+                pv[b][jj] = load16(a.peers + (j0 + jj) * slot_stride + base[b]);
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+              for (int jj = 0; jj < GS; ++jj)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                  s[b][2 * p] += bf16lo(pv[b][jj][p]);
+                  s[b][2 * p + 1] += bf16hi(pv[b][jj][p]);
+                }
+          }
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            if (!ok[b]) continue;
+            if (a.out_bf16) {
+              const u32x4 o = {pack_bf16x2(s[b][0], s[b][1]), pack_bf16x2(s[b][2], s[b][3]),
+                               pack_bf16x2(s[b][4], s[b][5]), pack_bf16x2(s[b][6], s[b][7])};
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + base[b]) = o;
+            } else {
+              float* dst = reinterpret_cast<float*>(a.out) + base[b];
+              *reinterpret_cast<f32x4*>(dst) = f32x4{s[b][0], s[b][1], s[b][2], s[b][3]};
+              *reinterpret_cast<f32x4*>(dst + 4) = f32x4{s[b][4], s[b][5], s[b][6], s[b][7]};
+            }
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+template <class C, int MODE, int GS>
+__global__ void __launch_bounds__(C::THREADS) pk_gemm_rs_fused(KArgs a) {
+  constexpr int S = C::STAGES;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[C::LDS0];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds2[S > 2 ? C::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds3[S > 3 ? C::STAGE_BYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
@@ -277,10 +512,17 @@ __global__ void __launch_bounds__(C::THREADS) gemm_rs_kernel(KArgs a) {
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
 
-  const int nk = (int)((a.K + C::BK - 1) / C::BK);
+  const int nk = (a.K + C::BK - 1) / C::BK;
+  Loader<C> ld;
+  ld.init(a, wave, lane);
+  Reader<C> rd;
+  rd.init(wm, wn, lane);
 
   for (long long s = w; s < a.total_tiles; s += G) {
     const TileCoord tc = tile_at(a.g, s);
+    const long long row0 = (long long)tc.shard * a.S + (long long)tc.t * C::BM;
+    const int rows_valid = a.S - tc.t * C::BM;
+    const int col0 = tc.u * C::BN;
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -290,67 +532,47 @@ __global__ void __launch_bounds__(C::THREADS) gemm_rs_kernel(KArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    u32x4 ra[C::A_PER_THREAD];
-    u32x4 rb[C::B_PER_THREAD][8];
     if (nk > 0) {
-      load_a<C>(a, tc, 0, tid, ra);
-      load_b<C>(a, tc, 0, tid, rb);
-      store_a<C>(lds, tid, ra);
-      store_b<C>(lds + C::A_CHUNKS, tid, rb);
-    }
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-      const int cur = ks & 1;
-      const bool more = ks + 1 < nk;
-      if (more) {
-        load_a<C>(a, tc, (ks + 1) * C::BK, tid, ra);
-        load_b<C>(a, tc, (ks + 1) * C::BK, tid, rb);
+      // prologue: stages 0 .. S-2
+      constexpr int NQ = C::LOADS;
+      ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), lds0, wave, rows_valid, col0);
+      if constexpr (S > 2)
+        ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), lds1, wave, rows_valid, col0);
+      if constexpr (S > 3)
+        ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), lds2, wave, rows_valid,
+                                 col0);
+      // Full wait: it also retires the previous tile's epilogue stores, so
+      // the partial waits inside the loop only ever see these loads, which
+      // complete in issue order.
+      wait_vm0();
+      __syncthreads();
+      // S steps per trip, step I multiplies buffer I and fills buffer
+      // (I + S - 1) % S with the stage S-1 ahead.  A last partial trip
+      // multiplies stages of zeros, which leaves the accumulators unchanged
+      // (they never hold -0).
+      for (int kq = 0; kq < nk; kq += S) {
+#define PK_STEP(I)                                                                          \
+  main_stage<C>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,            \
+                pick<(I)>(lds0, lds1, lds2, lds3), pick<((I) + S - 1) % S>(lds0, lds1, lds2, lds3), \
+                wave, rows_valid, col0, acc)
+        PK_STEP(0);
+        PK_STEP(1);
+        if constexpr (S > 2) PK_STEP(2);
+        if constexpr (S > 3) PK_STEP(3);
+#undef PK_STEP
       }
-      const u32x4* st = lds + cur * C::STAGE_CHUNKS;
-      mma_stage<C>(st, st + C::A_CHUNKS, wm, wn, lane, acc);
-      if (more) {
-        u32x4* nx = lds + (cur ^ 1) * C::STAGE_CHUNKS;
-        store_a<C>(nx, tid, ra);
-        store_b<C>(nx + C::A_CHUNKS, tid, rb);
-      }
+      wait_vm0();        // loads of stages past the end (zeros) into the staging area
       __syncthreads();
     }
 
-    // Epilogue: re-lay each 32-row stripe of the wave tile through LDS so
-    // that every lane owns 8 consecutive columns of one row (16-byte global
-    // accesses), then send, sum or store.
-    float* stage = lds_f + wave * 32 * C::EPI_STRIDE;
-    constexpr int LPR = C::WN / 8;                 // lanes per staged row
-    constexpr int ROWS_PER_IT = 64 / LPR;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          stage[row * C::EPI_STRIDE + fn * 32 + (lane & 31)] = acc[fm][fn][r];
-        }
-      __syncthreads();
-#pragma unroll
-      for (int it = 0; it < 32 / ROWS_PER_IT; ++it) {
-        const int rr = it * ROWS_PER_IT + lane / LPR;
-        const int c8 = lane % LPR;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
-        const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        const int lr = tc.t * C::BM + wm * C::WM + fm * 32 + rr;
-        const long long col = (long long)tc.u * C::BN + wn * C::WN + c8 * 8;
-        if (lr < a.S && col < a.N) emit8(a, tc, lr, col, v);
-      }
-      __syncthreads();
-    }
+    epilogue<C, MODE, GS>(a, tc, reinterpret_cast<float*>(lds0), wave, wm, wn, lane, acc);
 
-    if (!a.gemm_only && tc.shard != a.rank) {
+    if (MODE == kFused && tc.shard != a.rank) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();
       if (tid == 0) signal_chunks(a, tc, C::BM);
     }
+    __syncthreads();   // the staging area is the next tile's first stage
   }
 }
 
@@ -364,28 +586,38 @@ static const CfgInfo kCfgs[] = {
     {Cfg1::BM, Cfg1::BN, Cfg1::BK, Cfg1::WM, Cfg1::WN, Cfg1::THREADS},
     {Cfg2::BM, Cfg2::BN, Cfg2::BK, Cfg2::WM, Cfg2::WN, Cfg2::THREADS},
     {Cfg3::BM, Cfg3::BN, Cfg3::BK, Cfg3::WM, Cfg3::WN, Cfg3::THREADS},
+    {Cfg4::BM, Cfg4::BN, Cfg4::BK, Cfg4::WM, Cfg4::WN, Cfg4::THREADS},
+    {Cfg5::BM, Cfg5::BN, Cfg5::BK, Cfg5::WM, Cfg5::WN, Cfg5::THREADS},
 };
 static constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 static constexpr int kAssumedCUs = 256;   // MI355X; used only for the static pick
 
+// Column tiles per locality group: with 256 workgroups in flight and 32 per
+// XCD, groups of 8 columns give every XCD a 4 x 8 block of tiles at a time.
 static int default_group_n(const CfgInfo& c, int Tn) {
   (void)c;
-  return Tn;
+  return Tn < 8 ? Tn : 8;
 }
 
 static int select_config(long long M, long long N, long long K, int P) {
   (void)K;
   const long long S = P > 0 ? M / P : 0;
-  for (int i = 0; i < kNumCfgs; ++i) {
-    const CfgInfo& c = kCfgs[i];
+  static const int order[] = {1, 4, 2, 3};   // largest tile first
+  for (int id : order) {
+    const CfgInfo& c = kCfgs[id - 1];
     if (S < c.BM || N < c.BN) continue;
     const long long tiles = (long long)P * ((S + c.BM - 1) / c.BM) * ((N + c.BN - 1) / c.BN);
-    if (tiles >= 4LL * kAssumedCUs) return i + 1;
+    if (tiles >= kAssumedCUs) return id;
   }
-  return kNumCfgs;
+  return 3;
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Buffer-load offsets are 32-bit: an A row panel (256 rows x K) and 64 rows of
+// B must each stay below 2^31 bytes.
+static constexpr long long kMaxK = 1LL << 22;
+static constexpr long long kMaxN = 1LL << 24;
 
 static int validate(const void* A, const void* B, const void* peers, const void* send,
                     const void* out, const uint32_t* flags, long long M, long long N,
@@ -405,7 +637,7 @@ static int validate(const void* A, const void* B, const void* peers, const void*
       return PK_ERR_SHAPE;
     }
   }
-  if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31)) return PK_ERR_TOO_LARGE;
+  if (M > (1LL << 31) || N > kMaxN || K > kMaxK) return PK_ERR_TOO_LARGE;
   if (o && (o->config < 0 || o->config > kNumCfgs)) return PK_ERR_CONFIG;
   if (o && (o->max_workgroups < 0 || o->group_n < 0)) return PK_ERR_CONFIG;
   if (M == 0 || N == 0) return PK_OK;     // nothing to write
@@ -420,15 +652,16 @@ static int validate(const void* A, const void* B, const void* peers, const void*
   return PK_OK;
 }
 
-template <class C>
+// Resident workgroups per CU of one kernel instance, asked once per device.
+template <class C, int MODE, int GS>
 static int occupancy_of(int dev) {
   static int occ[64];
   static std::once_flag once[64];
   if (dev < 0 || dev >= 64) return 1;
   std::call_once(once[dev], [&] {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, gemm_rs_kernel<C>, C::THREADS, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pk_gemm_rs_fused<C, MODE, GS>,
+                                                     C::THREADS, 0) != hipSuccess ||
         blocks < 1)
       blocks = 1;
     occ[dev] = blocks;
@@ -449,8 +682,20 @@ static int cu_count(int dev) {
   return cus[dev];
 }
 
+template <class C, int MODE, int GS>
+static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_LAUNCH;
+  long long grid = (long long)cu_count(dev) * occupancy_of<C, MODE, GS>(dev);
+  if (o && o->max_workgroups > 0 && o->max_workgroups < grid) grid = o->max_workgroups;
+  if (grid > a.total_tiles) grid = a.total_tiles;
+  hipLaunchKernelGGL((pk_gemm_rs_fused<C, MODE, GS>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                     stream, a);
+  return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
+}
+
 template <class C>
-static int launch(KArgs& a, const pk_options* o, hipStream_t stream) {
+static int launch(KArgs& a, bool gemm_only, const pk_options* o, hipStream_t stream) {
   a.g.BM = C::BM;
   a.g.BN = C::BN;
   a.g.Tm = a.S > 0 ? ceil_div(a.S, C::BM) : 0;
@@ -458,13 +703,12 @@ static int launch(KArgs& a, const pk_options* o, hipStream_t stream) {
   a.g.group_n = (o && o->group_n > 0) ? o->group_n : default_group_n(kCfgs[0], a.g.Tn);
   a.total_tiles = a.g.total();
   if (a.total_tiles == 0) return PK_OK;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_LAUNCH;
-  long long grid = (long long)cu_count(dev) * occupancy_of<C>(dev);
-  if (o && o->max_workgroups > 0 && o->max_workgroups < grid) grid = o->max_workgroups;
-  if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL(gemm_rs_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
+  if (gemm_only) return launch_as<C, kGemmOnly, 1>(a, o, stream);
+  // peer slots summed per batch of loads: 7 for P = 8 (and 15, 22, ...)
+  const int np = a.P - 1;
+  if (np > 0 && np % 7 == 0) return launch_as<C, kFused, 7>(a, o, stream);
+  if (np > 0 && np % 3 == 0) return launch_as<C, kFused, 3>(a, o, stream);
+  return launch_as<C, kFused, 1>(a, o, stream);
 }
 
 static int run(const void* A, const void* B, const void* peers, void* send, void* out,
@@ -482,10 +726,10 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.out = out;
   a.flags = flags;
   a.M = M;
-  a.N = N;
-  a.K = K;
-  a.gemm_only = (o && o->gemm_only) ? 1 : 0;
-  if (a.gemm_only) {
+  a.N = (int)N;
+  a.K = (int)K;
+  const bool gemm_only = o && o->gemm_only;
+  if (gemm_only) {
     // One shard covering every row, nothing sent.
     a.P = 1;
     a.rank = 0;
@@ -509,9 +753,11 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg) {
-    case 1: return launch<Cfg1>(a, o, s);
-    case 2: return launch<Cfg2>(a, o, s);
-    case 3: return launch<Cfg3>(a, o, s);
+    case 1: return launch<Cfg1>(a, gemm_only, o, s);
+    case 2: return launch<Cfg2>(a, gemm_only, o, s);
+    case 3: return launch<Cfg3>(a, gemm_only, o, s);
+    case 4: return launch<Cfg4>(a, gemm_only, o, s);
+    case 5: return launch<Cfg5>(a, gemm_only, o, s);
     default: return PK_ERR_CONFIG;
   }
 }

@@ -57,13 +57,13 @@ MED = gen.Workload("medium", P=4, rank=1, M=1024, N=512, K=192, chunk_rows=64,
                    ab_dist="normal_sqrtk", peer_dist="normal", out_dtype="f32")
 
 
-@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("order", [0, 1, 2])
 def test_medium_integer_every_config_and_order(config, order):
     _run_and_check(MED, "f32", integer=True, order=order, config=config)
 
 
-@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_medium_real_every_config(config, out_dtype):
     _run_and_check(MED, out_dtype, integer=False, config=config)
@@ -75,7 +75,7 @@ RAGGED = gen.Workload("ragged", P=3, rank=2, M=600, N=328, K=136, chunk_rows=40,
                       ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
 
 
-@pytest.mark.parametrize("config", [1, 2, 3])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("integer", [True, False])
 def test_ragged_tails(config, integer):
     _run_and_check(RAGGED, "bf16", integer=integer, config=config)

@@ -103,12 +103,15 @@ def test_config_table():
 
 
 def test_select_config_for_the_workloads():
+    """The pick is the largest tile that still gives every CU (256) a tile."""
     big = pk.pk_config_info(pk.pk_select_config(32768, 32768, 4096, 8))
     assert big["BM"] == 256 and big["BN"] == 256
-    mid = pk.pk_config_info(pk.pk_select_config(4096, 4096, 512, 8))
-    assert mid["BM"] <= 512 // 4        # at least 4 row tiles per shard
-    tiny = pk.pk_config_info(pk.pk_select_config(256, 256, 128, 2))
-    assert tiny["BM"] <= 128
+    for M, N, K, P in ((4096, 4096, 512, 8), (256, 256, 128, 2), (2048, 1024, 64, 4)):
+        c = pk.pk_config_info(pk.pk_select_config(M, N, K, P))
+        tiles = P * -(-(M // P) // c["BM"]) * -(-N // c["BN"])
+        smaller = [pk.pk_config_info(i) for i in range(1, pk.pk_config_count() + 1)]
+        if tiles < 256:      # only the smallest tile may leave CUs idle
+            assert c["BM"] * c["BN"] == min(x["BM"] * x["BN"] for x in smaller)
 
 
 # ---------------------------------------------------------------- tile walk
@@ -138,13 +141,14 @@ def test_tile_orders_follow_their_definitions():
     M, N, P, rank, cfg = 4096, 4096, 8, 3, 2
     Tm, Tn = _tiles(M, N, P, cfg)
     per = Tm * Tn
-    rm = pk.pk_tile_walk(M, N, P, rank, cfg, 0)
+    # group_n = Tn: plain chunk-major order inside a shard
+    rm = pk.pk_tile_walk(M, N, P, rank, cfg, 0, group_n=Tn)
     assert list(rm[:, 0]) == [d for d in range(P) for _ in range(per)]
     # inside a shard: chunk-major (row tile outer, column tile inner)
     assert [tuple(x) for x in rm[:per, 1:]] == [(t, u) for t in range(Tm) for u in range(Tn)]
-    of = pk.pk_tile_walk(M, N, P, rank, cfg, 1)
+    of = pk.pk_tile_walk(M, N, P, rank, cfg, 1, group_n=Tn)
     assert list(of[:, 0]) == [(rank + i) % P for i in range(P) for _ in range(per)]
-    rr = pk.pk_tile_walk(M, N, P, rank, cfg, 2)
+    rr = pk.pk_tile_walk(M, N, P, rank, cfg, 2, group_n=Tn)
     assert list(rr[:P, 0]) == [(rank + 1 + i) % P for i in range(P)]
     assert rr[P - 1, 0] == rank                    # owned shard last in each round
     assert all(len(set(rr[i * P:(i + 1) * P, 0])) == P for i in range(per))
