@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--config", type=int, default=0)
     p.add_argument("--group-n", type=int, default=0)
     p.add_argument("--max-workgroups", type=int, default=0)
+    p.add_argument("--owned-split", type=int, default=0, choices=(-1, 0, 1),
+                   help="owned shard in 64x128 sub-tiles: 1 on, -1 off, 0 library default")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm-only", action="store_true")
@@ -88,6 +90,8 @@ def time_steps(fn, n_sets, warmup, steps, torch):
 def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_only=True,
             tile_order=None, chunk_rows=None):
     chunk = chunk_rows or args.chunk_rows or w.chunk_rows
+    if tile_order is None:
+        tile_order = args.tile_order
     order = w.tile_order if tile_order is None else tile_order
     set_bytes = w.algorithmic_bytes()
     n_sets = 1
@@ -96,6 +100,7 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
     sets = [BufferSet(w, 17 * i, chunk, torch, gen, pk) for i in range(n_sets)]
     out_bf16 = 1 if w.out_dtype == "bf16" else 0
     opts = dict(config=args.config, max_workgroups=args.max_workgroups, group_n=args.group_n)
+    fused_opts = dict(opts, owned_split=args.owned_split)
 
     def step(i, ev):
         s = sets[i]
@@ -103,7 +108,7 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         if ev:
             ev[0].record()
         pk.pk_gemm_rs_local_ex(s.A, s.B, s.peers, s.send, s.out, s.flags, w.M, w.N, w.K, w.P,
-                               w.rank, chunk, order, out_bf16, **opts)
+                               w.rank, chunk, order, out_bf16, **fused_opts)
         if ev:
             ev[1].record()
 

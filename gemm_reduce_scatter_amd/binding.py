@@ -28,7 +28,8 @@ class PkError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("config", ctypes.c_int), ("max_workgroups", ctypes.c_int),
-                ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int)]
+                ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int),
+                ("owned_split", ctypes.c_int), ("signal_batch", ctypes.c_int)]
 
 
 def lib_path() -> str:
@@ -64,7 +65,7 @@ def load():
     lib.pk_config_info.restype = i32
     lib.pk_select_config.argtypes = [i64, i64, i64, i32]
     lib.pk_select_config.restype = i32
-    lib.pk_tile_walk.argtypes = [i64, i64, i32, i32, i32, i32, i32,
+    lib.pk_tile_walk.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32,
                                  ctypes.POINTER(ctypes.c_int32), i64]
     lib.pk_tile_walk.restype = i64
     lib.pk_chunk_arrivals.argtypes = [i64, i64, i32, i32, i32, i32]
@@ -103,8 +104,10 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _opts(config=0, max_workgroups=0, group_n=0, gemm_only=False):
-    return _Options(int(config), int(max_workgroups), int(group_n), 1 if gemm_only else 0)
+def _opts(config=0, max_workgroups=0, group_n=0, gemm_only=False, owned_split=0,
+          signal_batch=0):
+    return _Options(int(config), int(max_workgroups), int(group_n), 1 if gemm_only else 0,
+                    int(owned_split), int(signal_batch))
 
 
 def _check_tensors(A, B, peer_partials, send_bufs, out, flags):
@@ -146,10 +149,11 @@ def pk_gemm_rs_local_bf16out(A, B, peer_partials, send_bufs, out, flags, M, N, K
 
 def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                         chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0,
-                        group_n=0, gemm_only=False, stream=None) -> int:
+                        group_n=0, gemm_only=False, owned_split=0, signal_batch=0,
+                        stream=None) -> int:
     """Fused share with explicit tile configuration / grid / grouping options."""
     _check_tensors(A, B, peer_partials, send_bufs, out, flags)
-    o = _opts(config, max_workgroups, group_n, gemm_only)
+    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
     return _check(load().pk_gemm_rs_local_ex(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
         int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
@@ -162,11 +166,11 @@ def pk_flags_words(P, M, chunk_rows) -> int:
 
 def pk_validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
                 tile_order, out_bf16=0, config=0, max_workgroups=0, group_n=0,
-                gemm_only=False) -> int:
+                gemm_only=False, owned_split=0, signal_batch=0) -> int:
     """Return code the library would give these arguments (no HIP call).
 
     Pointer arguments are plain integers (addresses) or None."""
-    o = _opts(config, max_workgroups, group_n, gemm_only)
+    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
     v = [None if p is None else ctypes.c_void_p(int(p)) for p in
          (A, B, peer_partials, send_bufs, out, flags)]
     return load().pk_validate(*v, int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),
@@ -187,15 +191,16 @@ def pk_select_config(M, N, K, P) -> int:
     return _check(load().pk_select_config(int(M), int(N), int(K), int(P)))
 
 
-def pk_tile_walk(M, N, P, rank, config, tile_order, group_n=0) -> np.ndarray:
-    """The tile walk as an int32 array [total, 3] of (shard, row tile, column tile)."""
+def pk_tile_walk(M, N, P, rank, config, tile_order, group_n=0, owned_split=0) -> np.ndarray:
+    """The work walk as an int32 array [total, 4] of (shard, row tile, column tile,
+    sub-tile); sub-tile is -1 for whole tiles."""
     lib = load()
     total = _check(lib.pk_tile_walk(int(M), int(N), int(P), int(rank), int(config),
-                                    int(tile_order), int(group_n), None, 0))
-    buf = np.zeros((max(total, 1), 3), dtype=np.int32)
+                                    int(tile_order), int(group_n), int(owned_split), None, 0))
+    buf = np.zeros((max(total, 1), 4), dtype=np.int32)
     _check(lib.pk_tile_walk(int(M), int(N), int(P), int(rank), int(config), int(tile_order),
-                            int(group_n), buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                            int(total)))
+                            int(group_n), int(owned_split),
+                            buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(total)))
     return buf[:total]
 
 

@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "pk_gemm_rs.h"
 #include "pk_plan.h"
@@ -87,7 +88,6 @@ struct Cfg {
   static_assert(B_LOADS >= 1 && B_BYTES % (1024 * WAVES) == 0, "B stage splits over the waves");
   static_assert(B_CPR >= 8 && B_CPR <= 64, "B row is 8..64 chunks");
   static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a CU");
-  static_assert(LOADS % KK == 0, "loads split over the k16 steps");
 };
 
 // id 1..5; the table in pk_config_info mirrors these.
@@ -96,6 +96,8 @@ using Cfg2 = Cfg<128, 128, 2, 2, 64, 2>;
 using Cfg3 = Cfg<64, 64, 2, 2, 64, 2>;
 using Cfg4 = Cfg<256, 128, 2, 2, 32, 4>;
 using Cfg5 = Cfg<256, 256, 2, 2, 64, 2>;
+// Owned sub-tiles of Cfg1 tiles when the owned shard is split (8 per tile).
+using CfgOwned = Cfg<64, 128, 2, 2, 64, 4>;
 
 struct KArgs {
   const uint16_t* A;
@@ -108,6 +110,7 @@ struct KArgs {
   int N, K;            // N <= 2^24, K <= 2^22 (validated)
   int P, rank, S, chunk_rows, n_chunks;
   int out_bf16;
+  int sig_batch;       // send tiles per ready-word release (>= 1)
   Grid g;
   long long total_tiles;
 };
@@ -146,6 +149,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, PK_LDS void* dst
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 16-byte store of output data (send chunks, the owned shard, GEMM-only C).
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -318,8 +326,10 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
                                             int col0, f32x16 (&acc)[C::FM][C::FN],
                                             typename Reader<C>::Frags (&f)[2]) {
   if constexpr (KKI < C::KK) {
-    constexpr int QP = C::LOADS / C::KK;
-    ld.template issue<KKI * QP, (KKI + 1) * QP>(a, ns, nxt, wave, rows_valid, col0);
+    constexpr int QP = (C::LOADS + C::KK - 1) / C::KK;   // loads issued per k16 step
+    constexpr int Q0 = KKI * QP < C::LOADS ? KKI * QP : C::LOADS;
+    constexpr int Q1 = (KKI + 1) * QP < C::LOADS ? (KKI + 1) * QP : C::LOADS;
+    ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
     if constexpr (KKI + 1 < C::KK) rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
     Reader<C>::mfma(f[KKI & 1], acc);
     stage_steps<C, KKI + 1>(a, ld, ns, rd, cur, nxt, wave, rows_valid, col0, acc, f);
@@ -356,12 +366,14 @@ __device__ __forceinline__ unsigned char* pick(unsigned char* b0, unsigned char*
   else return b3;
 }
 
-// Ready-word protocol for one finished send tile.  Every thread has already
-// made its stores visible device-wide (release fence) and the workgroup has
-// met at a barrier.  One thread then adds an arrival to each chunk the tile
-// touches; the arrival that completes a chunk (acquire-release on the
-// counter) publishes the ready word with a release store and resets the
-// counter for the next launch.
+// Ready-word protocol (the pages' signal primitive, per chunk).  A caller
+// has made the stores of one or more finished send tiles visible at device
+// scope with a release fence; for each tile it then adds one arrival to
+// every chunk the tile touches.  Each arrival is relaxed: the data it vouches
+// for was released before it.  The arrival that completes a chunk acquires
+// (so the other workgroups' released stores happen before what follows),
+// publishes the ready word with a release store and resets the counter for
+// the next launch.
 __device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& tc, int BM) {
   int c0, c1;
   chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
@@ -371,9 +383,10 @@ __device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& t
   for (int c = c0; c <= c1; ++c) {
     const int idx = slot * a.n_chunks + c;
     const uint32_t want = expected_arrivals(c, BM, a.chunk_rows, a.g.Tn);
-    const uint32_t old = __hip_atomic_fetch_add(&counters[idx], 1u, __ATOMIC_ACQ_REL,
+    const uint32_t old = __hip_atomic_fetch_add(&counters[idx], 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1u == want) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&counters[idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -383,29 +396,90 @@ __device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& t
 enum Mode : int { kFused = 0, kGemmOnly = 1 };
 
 // ---------------------------------------------------------------------------
-// Epilogue of one tile.  Each wave re-lays its accumulators, one 16-row half
-// of a 32-row stripe at a time, through LDS so that every lane owns 8
+// Epilogue of one work item.  Each wave re-lays its accumulators, one 16-row
+// half of a 32-row stripe at a time, through LDS so that every lane owns 8
 // consecutive columns of one row (16-byte global accesses), then sends, sums
-// or stores.
+// or stores.  `lrow0` is the shard-local row and `col0` the column of the
+// item's first element.
+//
+// Lane segments: for stripe fm, half h and pass it, a lane owns row
+// lrow0 + wm*WM + 32 fm + 16 h + it*RPI + lane/LPR, columns
+// col0 + wn*WN + 8 (lane%LPR) .. +7.
 // ---------------------------------------------------------------------------
-template <class C, int MODE, int GS>
-__device__ __forceinline__ void epilogue(const KArgs& a, const TileCoord& tc,
+template <class C>
+struct Seg {
+  static constexpr int LPR = C::WN / 8;        // lanes per staged row
+  static constexpr int RPI = 64 / LPR;         // rows per pass
+  static constexpr int PASSES = 16 / RPI;
+  static constexpr int COUNT = C::FM * 2 * PASSES;   // segments per lane
+  __device__ __forceinline__ static int row(int wm, int lane, int fm, int h, int it) {
+    return wm * C::WM + fm * 32 + 16 * h + it * RPI + lane / LPR;
+  }
+  __device__ __forceinline__ static int col(int wn, int lane) {
+    return wn * C::WN + (lane % LPR) * 8;
+  }
+};
+
+// Peer partials of every segment of an owned item, read into registers
+// before the main loop so the loads overlap it (GS = P-1 slots).
+template <class C, int GS>
+struct PeerPrefetch {
+  u32x4 v[Seg<C>::COUNT][GS];
+  __device__ __forceinline__ void load(const KArgs& a, int lrow0, int col0, int wm, int wn,
+                                       int lane) {
+    const long long slot_stride = (long long)a.S * a.N;
+    const int col = col0 + Seg<C>::col(wn, lane);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int it = 0; it < Seg<C>::PASSES; ++it) {
+          const int lr = lrow0 + Seg<C>::row(wm, lane, fm, h, it);
+          const bool ok = lr < a.S && col < a.N;
+          const long long base = ok ? (long long)lr * a.N + col : 0;   // row 0 stays in bounds
+          const int sg = (fm * 2 + h) * Seg<C>::PASSES + it;
+#pragma unroll
+          for (int jj = 0; jj < GS; ++jj) v[sg][jj] = load16(a.peers + jj * slot_stride + base);
+        }
+  }
+};
+
+template <int GS>
+struct NoPrefetch {};
+
+__device__ __forceinline__ void store_out(const KArgs& a, long long base, const float (&s)[8]) {
+  if (a.out_bf16) {
+    const u32x4 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+                     pack_bf16x2(s[6], s[7])};
+    store16(reinterpret_cast<uint16_t*>(a.out) + base, o);
+  } else {
+    float* dst = reinterpret_cast<float*>(a.out) + base;
+    store16(dst, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]),
+                       __float_as_uint(s[3])});
+    store16(dst + 4, u32x4{__float_as_uint(s[4]), __float_as_uint(s[5]), __float_as_uint(s[6]),
+                           __float_as_uint(s[7])});
+  }
+}
+
+template <class C, int MODE, int GS, class PF>
+__device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, int col0,
                                          float* lds_f, int wave, int wm, int wn, int lane,
-                                         f32x16 (&acc)[C::FM][C::FN]) {
+                                         f32x16 (&acc)[C::FM][C::FN], const PF& pf) {
+  using SG = Seg<C>;
+  constexpr bool PREF = !__is_same(PF, NoPrefetch<GS>);
   float* stage = lds_f + wave * 16 * C::EPI_STRIDE;
-  constexpr int LPR = C::WN / 8;                 // lanes per staged row
-  constexpr int RPI = 64 / LPR;                  // rows per pass
-  constexpr int PASSES = 16 / RPI;
+  constexpr int LPR = SG::LPR, RPI = SG::RPI, PASSES = SG::PASSES;
   // owned segments summed together: 4 for small wave tiles, 2 when the
   // accumulators take a large part of the register file
-  constexpr int BATCH = C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4);
+  constexpr int BATCH = PREF ? PASSES : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
   static_assert(PASSES % BATCH == 0, "batches tile the passes");
-  const bool owned = MODE == kFused && tc.shard == a.rank;
+  const bool owned = MODE == kFused && shard == a.rank;
   const int c8 = lane % LPR;
-  const long long col = (long long)tc.u * C::BN + wn * C::WN + c8 * 8;
+  const long long col = (long long)col0 + SG::col(wn, lane);
   const bool col_ok = col < a.N;
   const long long slot_stride = (long long)a.S * a.N;
-  const int slot = MODE == kFused && !owned ? slot_of(tc.shard, a.rank) : 0;
+  const int slot = MODE == kFused && !owned ? slot_of(shard, a.rank) : 0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
@@ -419,23 +493,22 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const TileCoord& tc,
           stage[row * C::EPI_STRIDE + fn * 32 + (lane & 31)] = acc[fm][fn][r];
         }
       wave_lds_sync();
-      const int lr0 = tc.t * C::BM + wm * C::WM + fm * 32 + 16 * h;   // shard-local row
       if (!owned) {
 #pragma unroll
         for (int it = 0; it < PASSES; ++it) {
           const int rr = it * RPI + lane / LPR;
           const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
           const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
-          const int lr = lr0 + rr;
+          const int lr = lrow0 + SG::row(wm, lane, fm, h, it);
           if (lr < a.S && col_ok) {
             const u32x4 o = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
                              pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
             uint16_t* dst;
             if (MODE == kGemmOnly)
-              dst = reinterpret_cast<uint16_t*>(a.out) + ((long long)tc.shard * a.S + lr) * a.N + col;
+              dst = reinterpret_cast<uint16_t*>(a.out) + ((long long)shard * a.S + lr) * a.N + col;
             else
               dst = a.send + (slot * (long long)a.S + lr) * a.N + col;
-            *reinterpret_cast<u32x4*>(dst) = o;
+            store16(dst, o);
           }
         }
       } else {
@@ -451,41 +524,46 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const TileCoord& tc,
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
             s[b][0] = x0[0]; s[b][1] = x0[1]; s[b][2] = x0[2]; s[b][3] = x0[3];
             s[b][4] = x1[0]; s[b][5] = x1[1]; s[b][6] = x1[2]; s[b][7] = x1[3];
-            const int lr = lr0 + rr;
+            const int lr = lrow0 + SG::row(wm, lane, fm, h, it0 + b);
             ok[b] = lr < a.S && col_ok;
             base[b] = ok[b] ? (long long)lr * a.N + col : 0;   // row 0 stays in bounds
           }
-          // ascending slot order; GS slots' loads are in flight together
-          for (int j0 = 0; j0 < a.P - 1; j0 += GS) {
-            u32x4 pv[BATCH][GS];
+          if constexpr (PREF) {
+            // slots 0 .. GS-1 = all P-1 peers, in ascending order
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b)
-#pragma unroll
-              for (int jj = 0; jj < GS; ++jj)
-                pv[b][jj] = load16(a.peers + (j0 + jj) * slot_stride + base[b]);
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b)
+            for (int b = 0; b < BATCH; ++b) {
+              const int sg = (fm * 2 + h) * PASSES + it0 + b;
 #pragma unroll
               for (int jj = 0; jj < GS; ++jj)
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                  s[b][2 * p] += bf16lo(pv[b][jj][p]);
-                  s[b][2 * p + 1] += bf16hi(pv[b][jj][p]);
+                  s[b][2 * p] += bf16lo(pf.v[sg][jj][p]);
+                  s[b][2 * p + 1] += bf16hi(pf.v[sg][jj][p]);
                 }
-          }
+            }
+          } else {
+            // ascending slot order; GS slots' loads are in flight together
+            for (int j0 = 0; j0 < a.P - 1; j0 += GS) {
+              u32x4 pv[BATCH][GS];
 #pragma unroll
-          for (int b = 0; b < BATCH; ++b) {
-            if (!ok[b]) continue;
-            if (a.out_bf16) {
-              const u32x4 o = {pack_bf16x2(s[b][0], s[b][1]), pack_bf16x2(s[b][2], s[b][3]),
-                               pack_bf16x2(s[b][4], s[b][5]), pack_bf16x2(s[b][6], s[b][7])};
-              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + base[b]) = o;
-            } else {
-              float* dst = reinterpret_cast<float*>(a.out) + base[b];
-              *reinterpret_cast<f32x4*>(dst) = f32x4{s[b][0], s[b][1], s[b][2], s[b][3]};
-              *reinterpret_cast<f32x4*>(dst + 4) = f32x4{s[b][4], s[b][5], s[b][6], s[b][7]};
+              for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+                for (int jj = 0; jj < GS; ++jj)
+                  pv[b][jj] = load16(a.peers + (j0 + jj) * slot_stride + base[b]);
+#pragma unroll
+              for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+                for (int jj = 0; jj < GS; ++jj)
+#pragma unroll
+                  for (int p = 0; p < 4; ++p) {
+                    s[b][2 * p] += bf16lo(pv[b][jj][p]);
+                    s[b][2 * p + 1] += bf16hi(pv[b][jj][p]);
+                  }
             }
           }
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b)
+            if (ok[b]) store_out(a, base[b], s[b]);
         }
       }
       wave_lds_sync();
@@ -493,18 +571,106 @@ __device__ __forceinline__ void epilogue(const KArgs& a, const TileCoord& tc,
   }
 }
 
-template <class C, int MODE, int GS>
-__global__ void __launch_bounds__(C::THREADS) pk_gemm_rs_fused(KArgs a) {
+// LDS of the kernel: a ring of up to four stage buffers shared by the tile
+// configurations it runs; buffer 0 also holds the epilogue staging area.
+template <class C1, class C2>
+struct LdsPlan {
+  static constexpr int mx(int x, int y) { return x > y ? x : y; }
+  static constexpr int B0 = mx(C1::LDS0, C2::LDS0);
+  static constexpr int BS = mx(C1::STAGE_BYTES, C2::STAGE_BYTES);
+  static constexpr int ST = mx(C1::STAGES, C2::STAGES);
+  static constexpr int B2 = ST > 2 ? BS : 16;
+  static constexpr int B3 = ST > 3 ? BS : 16;
+  static_assert(B0 + BS + B2 + B3 <= 160 * 1024, "fits the 160 KiB LDS of a CU");
+};
+
+// One work item: a tile of configuration C whose first row is shard-local
+// row `lrow0` of shard `shard` and whose first column is `col0`.
+template <class C, int MODE, int GS, bool PREF>
+__device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, int col0,
+                                        unsigned char* b0, unsigned char* b1, unsigned char* b2,
+                                        unsigned char* b3, int tid, int wave, int lane) {
   constexpr int S = C::STAGES;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[C::LDS0];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds2[S > 2 ? C::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds3[S > 3 ? C::STAGE_BYTES : 16];
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  Loader<C> ld;
+  ld.init(a, wave, lane);
+  Reader<C> rd;
+  rd.init(wm, wn, lane);
+  const long long row0 = (long long)shard * a.S + lrow0;
+  const int rows_valid = a.S - lrow0;
+  const int nk = (a.K + C::BK - 1) / C::BK;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // prologue: stages 0 .. S-2
+  constexpr int NQ = C::LOADS;
+  if (nk > 0) {
+    ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), b0, wave, rows_valid, col0);
+    if constexpr (S > 2)
+      ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave, rows_valid, col0);
+    if constexpr (S > 3)
+      ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave, rows_valid,
+                               col0);
+  }
+  using PFT = typename std::conditional<PREF, PeerPrefetch<C, GS>, NoPrefetch<GS>>::type;
+  PFT pf;
+  if (nk > 0) {
+    // Loads complete in issue order, so this leaves stages 1 .. S-2 in
+    // flight; older stores of the previous item are retired too.
+    wait_vm<(S - 2) * NQ>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  // Owned sub-items read their peer partials now; the loads must land by the
+  // end of the first step, one stage of MFMA later.
+  if constexpr (PREF) pf.load(a, lrow0, col0, wm, wn, lane);
+  if (nk > 0) {
+    // S steps per trip, step I multiplies buffer I and fills buffer
+    // (I + S - 1) % S with the stage S-1 ahead.  A last partial trip
+    // multiplies stages of zeros, which leaves the accumulators unchanged
+    // (they never hold -0).
+    for (int kq = 0; kq < nk; kq += S) {
+#define PK_STEP(I)                                                                           \
+  main_stage<C>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,             \
+                pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3), wave,   \
+                rows_valid, col0, acc)
+      PK_STEP(0);
+      PK_STEP(1);
+      if constexpr (S > 2) PK_STEP(2);
+      if constexpr (S > 3) PK_STEP(3);
+#undef PK_STEP
+    }
+    wait_vm0();        // loads of stages past the end (zeros) into the staging area
+    __syncthreads();
+  }
+
+  epilogue<C, MODE, GS, PFT>(a, shard, lrow0, col0, reinterpret_cast<float*>(b0), wave, wm, wn,
+                             lane, acc, pf);
+}
+
+// The persistent kernel: workgroup w takes walk positions w, w+G, w+2G, ...
+// Whole tiles use configuration CS; owned sub-tiles (owned split R > 1) use
+// the smaller CO, with the peer partials read ahead into registers.
+template <class CS, class CO, int MODE, int GS>
+__global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
+  using L = LdsPlan<CS, CO>;
+  constexpr bool SPLIT = !__is_same(CS, CO);
+  static_assert(CS::THREADS == CO::THREADS, "one workgroup size");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[L::B0];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[L::BS];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds2[L::B2];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds3[L::B3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous run of walk positions.
@@ -512,67 +678,38 @@ __global__ void __launch_bounds__(C::THREADS) pk_gemm_rs_fused(KArgs a) {
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
 
-  const int nk = (a.K + C::BK - 1) / C::BK;
-  Loader<C> ld;
-  ld.init(a, wave, lane);
-  Reader<C> rd;
-  rd.init(wm, wn, lane);
-
+  // Finished send tiles are signalled in batches: one device-scope release
+  // (an L2 writeback on this multi-XCD part, several microseconds) covers up
+  // to a.sig_batch tiles.  Positions fs, fs+G, ..., up to the current one
+  // hold the tiles not yet signalled.
+  long long fs = w;
+  int npend = 0;
   for (long long s = w; s < a.total_tiles; s += G) {
     const TileCoord tc = tile_at(a.g, s);
-    const long long row0 = (long long)tc.shard * a.S + (long long)tc.t * C::BM;
-    const int rows_valid = a.S - tc.t * C::BM;
-    const int col0 = tc.u * C::BN;
-
-    f32x16 acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    if (nk > 0) {
-      // prologue: stages 0 .. S-2
-      constexpr int NQ = C::LOADS;
-      ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), lds0, wave, rows_valid, col0);
-      if constexpr (S > 2)
-        ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), lds1, wave, rows_valid, col0);
-      if constexpr (S > 3)
-        ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), lds2, wave, rows_valid,
-                                 col0);
-      // Full wait: it also retires the previous tile's epilogue stores, so
-      // the partial waits inside the loop only ever see these loads, which
-      // complete in issue order.
-      wait_vm0();
+    if (!SPLIT || tc.sub < 0) {
+      process<CS, MODE, GS, false>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1, lds2,
+                                   lds3, tid, wave, lane);
+      if (MODE == kFused && tc.shard != a.rank) ++npend;
+    } else if constexpr (SPLIT) {
+      const int sm = tc.sub / a.g.Rn, sn = tc.sub - sm * a.g.Rn;
+      process<CO, MODE, GS, true>(a, tc.shard, tc.t * CS::BM + sm * CO::BM,
+                                  tc.u * CS::BN + sn * CO::BN, lds0, lds1, lds2, lds3, tid, wave,
+                                  lane);
+    }
+    if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || s + G >= a.total_tiles)) {
+      wait_vm0();            // this thread's stores have reached the cache
       __syncthreads();
-      // S steps per trip, step I multiplies buffer I and fills buffer
-      // (I + S - 1) % S with the stage S-1 ahead.  A last partial trip
-      // multiplies stages of zeros, which leaves the accumulators unchanged
-      // (they never hold -0).
-      for (int kq = 0; kq < nk; kq += S) {
-#define PK_STEP(I)                                                                          \
-  main_stage<C>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,            \
-                pick<(I)>(lds0, lds1, lds2, lds3), pick<((I) + S - 1) % S>(lds0, lds1, lds2, lds3), \
-                wave, rows_valid, col0, acc)
-        PK_STEP(0);
-        PK_STEP(1);
-        if constexpr (S > 2) PK_STEP(2);
-        if constexpr (S > 3) PK_STEP(3);
-#undef PK_STEP
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
+        for (long long s2 = fs; s2 <= s; s2 += G) {
+          const TileCoord t2 = tile_at(a.g, s2);
+          if (t2.shard != a.rank) signal_chunks(a, t2, CS::BM);
+        }
       }
-      wait_vm0();        // loads of stages past the end (zeros) into the staging area
-      __syncthreads();
+      fs = s + G;
+      npend = 0;
     }
-
-    epilogue<C, MODE, GS>(a, tc, reinterpret_cast<float*>(lds0), wave, wm, wn, lane, acc);
-
-    if (MODE == kFused && tc.shard != a.rank) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0) signal_chunks(a, tc, C::BM);
-    }
-    __syncthreads();   // the staging area is the next tile's first stage
+    __syncthreads();   // the staging area is the next item's first stage
   }
 }
 
@@ -591,6 +728,7 @@ static const CfgInfo kCfgs[] = {
 };
 static constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 static constexpr int kAssumedCUs = 256;   // MI355X; used only for the static pick
+static constexpr int kDefaultSignalBatch = 8;
 
 // Column tiles per locality group: with 256 workgroups in flight and 32 per
 // XCD, groups of 8 columns give every XCD a 4 x 8 block of tiles at a time.
@@ -640,6 +778,8 @@ static int validate(const void* A, const void* B, const void* peers, const void*
   if (M > (1LL << 31) || N > kMaxN || K > kMaxK) return PK_ERR_TOO_LARGE;
   if (o && (o->config < 0 || o->config > kNumCfgs)) return PK_ERR_CONFIG;
   if (o && (o->max_workgroups < 0 || o->group_n < 0)) return PK_ERR_CONFIG;
+  if (o && (o->owned_split < -1 || o->owned_split > 1)) return PK_ERR_CONFIG;
+  if (o && o->signal_batch < 0) return PK_ERR_CONFIG;
   if (M == 0 || N == 0) return PK_OK;     // nothing to write
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };
   if (!need(out)) return PK_ERR_POINTER;
@@ -653,15 +793,15 @@ static int validate(const void* A, const void* B, const void* peers, const void*
 }
 
 // Resident workgroups per CU of one kernel instance, asked once per device.
-template <class C, int MODE, int GS>
+template <class CS, class CO, int MODE, int GS>
 static int occupancy_of(int dev) {
   static int occ[64];
   static std::once_flag once[64];
   if (dev < 0 || dev >= 64) return 1;
   std::call_once(once[dev], [&] {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pk_gemm_rs_fused<C, MODE, GS>,
-                                                     C::THREADS, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pk_gemm_rs_fused<CS, CO, MODE, GS>,
+                                                     CS::THREADS, 0) != hipSuccess ||
         blocks < 1)
       blocks = 1;
     occ[dev] = blocks;
@@ -682,33 +822,60 @@ static int cu_count(int dev) {
   return cus[dev];
 }
 
-template <class C, int MODE, int GS>
+template <class CS, class CO, int MODE, int GS>
 static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_LAUNCH;
-  long long grid = (long long)cu_count(dev) * occupancy_of<C, MODE, GS>(dev);
+  long long grid = (long long)cu_count(dev) * occupancy_of<CS, CO, MODE, GS>(dev);
   if (o && o->max_workgroups > 0 && o->max_workgroups < grid) grid = o->max_workgroups;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL((pk_gemm_rs_fused<C, MODE, GS>), dim3((unsigned)grid), dim3(C::THREADS), 0,
-                     stream, a);
+  hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS>), dim3((unsigned)grid),
+                     dim3(CS::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
 }
 
+// Owned split of configuration `cfg` for a call: on request, or by default
+// when the whole-tile walk gives fewer than two tiles per CU (the owned
+// tiles then sit on the critical path).  Available for configuration 1 with
+// P - 1 in {1, 3, 7} (all peer slots are read ahead in one batch).
+static bool use_owned_split(int cfg, int P, long long whole_tiles, const pk_options* o) {
+  const int req = o ? o->owned_split : 0;
+  const bool able = cfg == 1 && (P == 2 || P == 4 || P == 8);
+  if (req < 0 || !able) return false;
+  if (req > 0) return true;
+  return whole_tiles < 2LL * kAssumedCUs;
+}
+
 template <class C>
-static int launch(KArgs& a, bool gemm_only, const pk_options* o, hipStream_t stream) {
+static int launch(KArgs& a, bool gemm_only, int cfg, const pk_options* o, hipStream_t stream) {
   a.g.BM = C::BM;
   a.g.BN = C::BN;
   a.g.Tm = a.S > 0 ? ceil_div(a.S, C::BM) : 0;
   a.g.Tn = ceil_div(a.N, C::BN);
   a.g.group_n = (o && o->group_n > 0) ? o->group_n : default_group_n(kCfgs[0], a.g.Tn);
+  a.g.Rm = a.g.Rn = 1;
+  const bool split = !gemm_only && use_owned_split(cfg, a.P, a.g.total(), o);
+  if (split) {
+    a.g.Rm = C::BM / CfgOwned::BM;
+    a.g.Rn = C::BN / CfgOwned::BN;
+  }
   a.total_tiles = a.g.total();
   if (a.total_tiles == 0) return PK_OK;
-  if (gemm_only) return launch_as<C, kGemmOnly, 1>(a, o, stream);
+  if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
+  if constexpr (__is_same(C, Cfg1)) {
+    if (split) {
+      switch (a.P - 1) {
+        case 7: return launch_as<C, CfgOwned, kFused, 7>(a, o, stream);
+        case 3: return launch_as<C, CfgOwned, kFused, 3>(a, o, stream);
+        default: return launch_as<C, CfgOwned, kFused, 1>(a, o, stream);
+      }
+    }
+  }
   // peer slots summed per batch of loads: 7 for P = 8 (and 15, 22, ...)
   const int np = a.P - 1;
-  if (np > 0 && np % 7 == 0) return launch_as<C, kFused, 7>(a, o, stream);
-  if (np > 0 && np % 3 == 0) return launch_as<C, kFused, 3>(a, o, stream);
-  return launch_as<C, kFused, 1>(a, o, stream);
+  if (np > 0 && np % 7 == 0) return launch_as<C, C, kFused, 7>(a, o, stream);
+  if (np > 0 && np % 3 == 0) return launch_as<C, C, kFused, 3>(a, o, stream);
+  return launch_as<C, C, kFused, 1>(a, o, stream);
 }
 
 static int run(const void* A, const void* B, const void* peers, void* send, void* out,
@@ -750,14 +917,15 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.g.S = a.S;
   a.g.N = (int)N;
   a.g.order = tile_order;
+  a.sig_batch = (o && o->signal_batch > 0) ? o->signal_batch : kDefaultSignalBatch;
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg) {
-    case 1: return launch<Cfg1>(a, gemm_only, o, s);
-    case 2: return launch<Cfg2>(a, gemm_only, o, s);
-    case 3: return launch<Cfg3>(a, gemm_only, o, s);
-    case 4: return launch<Cfg4>(a, gemm_only, o, s);
-    case 5: return launch<Cfg5>(a, gemm_only, o, s);
+    case 1: return launch<Cfg1>(a, gemm_only, cfg, o, s);
+    case 2: return launch<Cfg2>(a, gemm_only, cfg, o, s);
+    case 3: return launch<Cfg3>(a, gemm_only, cfg, o, s);
+    case 4: return launch<Cfg4>(a, gemm_only, cfg, o, s);
+    case 5: return launch<Cfg5>(a, gemm_only, cfg, o, s);
     default: return PK_ERR_CONFIG;
   }
 }
@@ -828,11 +996,12 @@ int pk_select_config(int64_t M, int64_t N, int64_t K, int P) {
 }
 
 int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,
-                     int group_n, int32_t* out3, int64_t cap) {
+                     int group_n, int owned_split, int32_t* out4, int64_t cap) {
   if (P < 1 || P > 64 || rank < 0 || rank >= P) return PK_ERR_RANK;
   if (tile_order < 0 || tile_order > 2) return PK_ERR_TILE_ORDER;
   if (M < 0 || N < 0 || M % P != 0) return PK_ERR_SHAPE;
   if (config < 1 || config > pk::kNumCfgs) return PK_ERR_CONFIG;
+  if (owned_split < 0 || (owned_split > 0 && config != 1)) return PK_ERR_CONFIG;
   const pk::CfgInfo& c = pk::kCfgs[config - 1];
   pk::Grid g;
   g.P = P;
@@ -845,12 +1014,15 @@ int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile
   g.Tn = pk::ceil_div(N, c.BN);
   g.order = tile_order;
   g.group_n = group_n > 0 ? group_n : pk::default_group_n(c, g.Tn);
+  g.Rm = owned_split ? pk::Cfg1::BM / pk::CfgOwned::BM : 1;
+  g.Rn = owned_split ? pk::Cfg1::BN / pk::CfgOwned::BN : 1;
   const long long total = g.total();
   for (long long s = 0; s < total && s < cap; ++s) {
     const pk::TileCoord tc = pk::tile_at(g, s);
-    out3[3 * s] = tc.shard;
-    out3[3 * s + 1] = tc.t;
-    out3[3 * s + 2] = tc.u;
+    out4[4 * s] = tc.shard;
+    out4[4 * s + 1] = tc.t;
+    out4[4 * s + 2] = tc.u;
+    out4[4 * s + 3] = tc.sub;
   }
   return total;
 }

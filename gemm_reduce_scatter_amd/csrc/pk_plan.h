@@ -16,14 +16,23 @@
 // raised by the last tile that writes into it, so the number of arrivals a
 // chunk waits for is (row tiles overlapping it) x Tn.
 //
-// Tile orders (the order tiles are handed out; results never depend on it,
-// Syncopate section 5.2 "Tile-Scheduler Swizzling" reorders waves the same
+// Owned split: the owned shard may be tiled finer than the send shards.
+// Every owned tile is then cut into R = Rm x Rn sub-tiles of (BM/Rm) x
+// (BN/Rn), each its own work item, so that the heavy owned epilogue (it
+// reads P-1 staged partials per element) is spread over many workgroups
+// instead of falling on the few that hold whole owned tiles.  R = 1 keeps
+// whole tiles.
+//
+// Tile orders (the order work items are handed out; results never depend on
+// it, Syncopate section 5.2 "Tile-Scheduler Swizzling" reorders waves the same
 // way without moving data):
 //   0 row-major:        shards 0 .. P-1, each shard chunk-major;
 //   1 owned-first:      shards rank, rank+1, ..., rank+P-1 (mod P);
-//   2 dest-round-robin: position s takes tile s/P of shard (rank+1+s) mod P,
-//                       so consecutive tiles go to different destinations and
-//                       the owned shard comes last in every round.
+//   2 dest-round-robin: round i holds tile i of shards rank+1, ...,
+//                       rank+P-1 (one per destination) followed by the R
+//                       items of owned tile i, so consecutive tiles go to
+//                       different destinations and the owned shard comes
+//                       last in every round.
 #pragma once
 #include <stdint.h>
 
@@ -41,12 +50,15 @@ struct TileCoord {
   int shard;   // owning rank of the tile's rows
   int t;       // shard-local row-tile index
   int u;       // column-tile index
+  int sub;     // -1: the whole tile; else owned sub-tile index in [0, Rm*Rn)
 };
 
 struct Grid {
   int P, rank, S, N, BM, BN, Tm, Tn, order, group_n;
+  int Rm, Rn;  // owned split (1 x 1: none)
   PK_HD long long tiles_per_shard() const { return (long long)Tm * Tn; }
-  PK_HD long long total() const { return tiles_per_shard() * P; }
+  PK_HD int R() const { return Rm * Rn; }
+  PK_HD long long total() const { return tiles_per_shard() * (P - 1 + R()); }
 };
 
 PK_HD int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -67,21 +79,42 @@ PK_HD void intra_shard(const Grid& g, long long i, int& t, int& u) {
   u = u0 + (int)(r - (long long)t * width);
 }
 
+// Work item at walk position s (0 <= s < total()).
 PK_HD TileCoord tile_at(const Grid& g, long long s) {
   TileCoord c;
   const long long per = g.tiles_per_shard();
-  long long i;
+  const int R = g.R();
+  long long i;       // tile index inside its shard
+  int sub = -1;      // owned sub-tile
   if (g.order == kDestRoundRobin) {
-    c.shard = (int)((g.rank + 1 + s % g.P) % g.P);
-    i = s / g.P;
-  } else if (g.order == kOwnedFirst) {
-    c.shard = (int)((g.rank + s / per) % g.P);
-    i = s % per;
+    const long long L = g.P - 1 + R;                      // items per round
+    i = s / L;
+    const int j = (int)(s - i * L);
+    if (j < g.P - 1) {
+      c.shard = (g.rank + 1 + j) % g.P;
+    } else {
+      c.shard = g.rank;
+      sub = j - (g.P - 1);
+    }
   } else {
-    c.shard = (int)(s / per);
-    i = s % per;
+    // shards in walk order; the owned one takes R * per positions
+    const int first = g.order == kOwnedFirst ? g.rank : 0;
+    const long long own_start =
+        g.order == kOwnedFirst ? 0 : (long long)g.rank * per;   // positions before the owned block
+    if (s >= own_start && s < own_start + R * per) {
+      c.shard = g.rank;
+      const long long q = s - own_start;
+      i = q / R;
+      sub = (int)(q - i * R);
+    } else {
+      const long long q = s < own_start ? s : s - (long long)(R - 1) * per;
+      const int k = (int)(q / per);                           // k-th shard in walk order
+      c.shard = (first + k) % g.P;
+      i = q - (long long)k * per;
+    }
   }
   intra_shard(g, i, c.t, c.u);
+  c.sub = (c.shard == g.rank && R > 1) ? sub : -1;
   return c;
 }
 

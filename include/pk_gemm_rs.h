@@ -92,6 +92,15 @@ typedef struct pk_options {
   int gemm_only;        /* 1: store bf16(A*B) for all M rows into `out` (bf16 [M][N]);
                            no send, peers or flags.  The standalone-GEMM reference
                            the fused kernel is measured against. */
+  int owned_split;      /* owned shard tiled finer than the send shards, so its
+                           epilogue (P-1 peer reads per element) spreads over many
+                           workgroups: 1 on, -1 off, 0 = auto (on when the walk has
+                           fewer than two whole tiles per CU).  Tile configuration 1
+                           with P in {2, 4, 8} only; elsewhere it stays off. */
+  int signal_batch;     /* finished send tiles of a workgroup whose chunk arrivals
+                           share one device-scope release, 0 = auto (8).  Larger
+                           batches cost fewer cache writebacks and raise ready words
+                           later; the last batch of a workgroup is always flushed. */
 } pk_options;
 
 /* The fused share with explicit options; out_bf16 selects bf16 (1) or fp32 (0)
@@ -121,12 +130,14 @@ int pk_config_info(int id, int* BM, int* BN, int* BK, int* WM, int* WN, int* thr
 /* Configuration id the library picks for a shape when opts->config == 0. */
 int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
 
-/* Host copy of the tile walk (host only): writes, for each of the first
- * min(cap, total) positions, the triple (shard, row tile, column tile) into
- * out3[3*i .. 3*i+2].  Returns the total number of tiles or a negative code.
- * group_n as in pk_options (0 = auto for this config). */
+/* Host copy of the work walk (host only): writes, for each of the first
+ * min(cap, total) positions, (shard, row tile, column tile, sub-tile) into
+ * out4[4*i .. 4*i+3]; sub-tile is -1 for a whole tile and 0..R-1 for the R
+ * sub-tiles of an owned tile under the owned split (owned_split = 1; only
+ * configuration 1).  Returns the total number of work items or a negative
+ * code.  group_n as in pk_options (0 = auto for this config). */
 int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,
-                     int group_n, int32_t* out3, int64_t cap);
+                     int group_n, int owned_split, int32_t* out4, int64_t cap);
 
 /* Arrival count chunk c of every slot waits for, under configuration `config`. */
 int64_t pk_chunk_arrivals(int64_t M, int64_t N, int P, int chunk_rows, int config, int c);

@@ -82,6 +82,39 @@ def test_ragged_tails(config, integer):
     _run_and_check(RAGGED.with_(rank=0), "f32", integer=integer, config=config, order=2)
 
 
+# The owned split: owned tiles of configuration 1 cut into 64 x 128 sub-tiles
+# whose peer partials are read ahead; P = 8, 4 and 2 use 7, 3 and 1 slots.
+SPLIT8 = gen.Workload("split8", P=8, rank=5, M=4096, N=768, K=200, chunk_rows=64,
+                      ab_dist="normal_sqrtk", peer_dist="normal", out_dtype="f32")
+SPLIT4 = gen.Workload("split4", P=4, rank=1, M=1200, N=328, K=136, chunk_rows=60,
+                      ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+SPLIT2 = gen.Workload("split2", P=2, rank=1, M=520, N=264, K=64, chunk_rows=52,
+                      ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("w", [SPLIT8, SPLIT4, SPLIT2], ids=lambda w: w.name)
+def test_owned_split_integer(w, order):
+    _run_and_check(w, "f32", integer=True, order=order, config=1, owned_split=1)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("w", [SPLIT8, SPLIT4, SPLIT2], ids=lambda w: w.name)
+def test_owned_split_real(w, out_dtype):
+    _run_and_check(w, out_dtype, integer=False, order=2, config=1, owned_split=1)
+
+
+def test_owned_split_matches_whole_tiles_bitwise():
+    A, B, peers = gen.make_inputs(SPLIT8, DEV, seed=11)
+    outs = []
+    for split in (-1, 1):
+        share = H.Share(SPLIT8, "f32")
+        H.run(share, A, B, peers, config=1, owned_split=split)
+        torch.cuda.synchronize()
+        outs.append((share.send.view(torch.int16).clone(), share.out.view(torch.int32).clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 @pytest.mark.parametrize("chunk_rows", [8, 40, 200])
 def test_chunk_sizes_ragged(chunk_rows):
     _run_and_check(RAGGED, "f32", integer=True, chunk_rows=chunk_rows)
@@ -178,9 +211,10 @@ def test_outputs_invariant_across_orders_chunks_and_runs():
     ref = None
     for chunk in (64, 128, 256, 512):
         for order in (0, 1, 2):
-            for grid in (0, 37):
+            for grid, split, sig in ((0, 0, 0), (37, 0, 1), (0, -1, 3), (100, 1, 1000)):
                 share = H.Share(CD, "f32", chunk_rows=chunk)
-                H.run(share, A, B, peers, tile_order=order, max_workgroups=grid)
+                H.run(share, A, B, peers, tile_order=order, max_workgroups=grid,
+                      owned_split=split, signal_batch=sig)
                 torch.cuda.synchronize()
                 assert torch.equal(share.flags.cpu(), torch.from_numpy(
                     H.expected_flags(CD, chunk).view(np.int32)))
@@ -188,7 +222,7 @@ def test_outputs_invariant_across_orders_chunks_and_runs():
                 if ref is None:
                     ref = cur
                 else:
-                    assert torch.equal(cur[0], ref[0]), (chunk, order, grid)
+                    assert torch.equal(cur[0], ref[0]), (chunk, order, grid, split)
                     assert torch.equal(cur[1].view(torch.int32), ref[1].view(torch.int32))
     # a repeat call on the same buffers after re-zeroing the flags
     share = H.Share(CD, "f32")

@@ -64,7 +64,7 @@ def _v(**kw):
                           args["rank"], args["chunk_rows"], args["tile_order"],
                           args.get("out_bf16", 0), args.get("config", 0),
                           args.get("max_workgroups", 0), args.get("group_n", 0),
-                          args.get("gemm_only", False))
+                          args.get("gemm_only", False), args.get("owned_split", 0))
 
 
 def test_validate_accepts_good_arguments():
@@ -85,7 +85,7 @@ def test_validate_accepts_good_arguments():
     (dict(chunk_rows=0), -2), (dict(M=-2), -2), (dict(out_bf16=2), -2),
     (dict(P=0), -3), (dict(rank=2), -3), (dict(rank=-1), -3), (dict(P=65, M=65 * 64), -3),
     (dict(tile_order=3), -4), (dict(tile_order=-1), -4),
-    (dict(config=99), -5), (dict(max_workgroups=-1), -5),
+    (dict(config=99), -5), (dict(max_workgroups=-1), -5), (dict(owned_split=2), -5),
 ])
 def test_validate_rejects(kw, code):
     assert _v(**kw) == code
@@ -132,9 +132,9 @@ def test_tile_walk_is_a_permutation(order, shape, group_n):
     M, N, P, rank, cfg = shape
     Tm, Tn = _tiles(M, N, P, cfg)
     w = pk.pk_tile_walk(M, N, P, rank, cfg, order, group_n)
-    assert w.shape == (P * Tm * Tn, 3)
+    assert w.shape == (P * Tm * Tn, 4)
     keys = {tuple(r) for r in w.tolist()}
-    assert keys == {(d, t, u) for d in range(P) for t in range(Tm) for u in range(Tn)}
+    assert keys == {(d, t, u, -1) for d in range(P) for t in range(Tm) for u in range(Tn)}
 
 
 def test_tile_orders_follow_their_definitions():
@@ -145,14 +145,14 @@ def test_tile_orders_follow_their_definitions():
     rm = pk.pk_tile_walk(M, N, P, rank, cfg, 0, group_n=Tn)
     assert list(rm[:, 0]) == [d for d in range(P) for _ in range(per)]
     # inside a shard: chunk-major (row tile outer, column tile inner)
-    assert [tuple(x) for x in rm[:per, 1:]] == [(t, u) for t in range(Tm) for u in range(Tn)]
+    assert [tuple(x) for x in rm[:per, 1:3]] == [(t, u) for t in range(Tm) for u in range(Tn)]
     of = pk.pk_tile_walk(M, N, P, rank, cfg, 1, group_n=Tn)
     assert list(of[:, 0]) == [(rank + i) % P for i in range(P) for _ in range(per)]
     rr = pk.pk_tile_walk(M, N, P, rank, cfg, 2, group_n=Tn)
     assert list(rr[:P, 0]) == [(rank + 1 + i) % P for i in range(P)]
     assert rr[P - 1, 0] == rank                    # owned shard last in each round
     assert all(len(set(rr[i * P:(i + 1) * P, 0])) == P for i in range(per))
-    assert np.array_equal(rr[::P, 1:], rm[:per, 1:])
+    assert np.array_equal(rr[::P, 1:3], rm[:per, 1:3])
 
 
 def test_grouped_walk_visits_column_groups():
@@ -161,6 +161,47 @@ def test_grouped_walk_visits_column_groups():
     w = pk.pk_tile_walk(M, N, P, rank, cfg, 0, group_n=4)
     first = w[:Tm * 4]
     assert set(first[:, 2]) == {0, 1, 2, 3} and set(first[:, 1]) == set(range(Tm))
+
+
+OWNED_R = 8          # owned sub-tiles per whole tile of configuration 1
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("shape", [(4096, 4096, 8, 3), (2048, 768, 4, 0), (600, 520, 2, 1)])
+def test_owned_split_walk_covers_every_item_once(order, shape):
+    M, N, P, rank = shape
+    Tm, Tn = _tiles(M, N, P, 1)
+    w = pk.pk_tile_walk(M, N, P, rank, 1, order, 0, owned_split=1)
+    assert w.shape == ((P - 1 + OWNED_R) * Tm * Tn, 4)
+    keys = [tuple(r) for r in w.tolist()]
+    assert len(set(keys)) == len(keys)
+    want = {(d, t, u, -1) for d in range(P) if d != rank for t in range(Tm) for u in range(Tn)}
+    want |= {(rank, t, u, q) for t in range(Tm) for u in range(Tn) for q in range(OWNED_R)}
+    assert set(keys) == want
+
+
+def test_owned_split_orders():
+    M, N, P, rank = 4096, 4096, 8, 3
+    Tm, Tn = _tiles(M, N, P, 1)
+    per = Tm * Tn
+    rm = pk.pk_tile_walk(M, N, P, rank, 1, 0, owned_split=1)
+    shards = list(rm[:, 0])
+    # row-major: shards in order, the owned block R times as long
+    expect = [d for d in range(P) for _ in range(per * (OWNED_R if d == rank else 1))]
+    assert shards == expect
+    own = rm[rank * per:rank * per + OWNED_R * per]
+    assert list(own[:OWNED_R, 3]) == list(range(OWNED_R))           # sub-tiles of one tile together
+    assert len({tuple(x) for x in own[:OWNED_R, 1:3]}) == 1
+    of = pk.pk_tile_walk(M, N, P, rank, 1, 1, owned_split=1)
+    assert set(of[:OWNED_R * per, 0]) == {rank}
+    rr = pk.pk_tile_walk(M, N, P, rank, 1, 2, owned_split=1)
+    L = P - 1 + OWNED_R
+    for i in range(3):                                               # round i
+        rnd = rr[i * L:(i + 1) * L]
+        assert list(rnd[:P - 1, 0]) == [(rank + 1 + j) % P for j in range(P - 1)]
+        assert set(rnd[P - 1:, 0]) == {rank} and list(rnd[P - 1:, 3]) == list(range(OWNED_R))
+    with pytest.raises(pk.PkError):
+        pk.pk_tile_walk(M, N, P, rank, 2, 0, owned_split=1)          # configuration 1 only
 
 
 # ---------------------------------------------------------------- chunk arrivals
