@@ -7,13 +7,22 @@ one batch of synthetic inputs resident in HBM.  Prints ONE JSON line.
 Default workload: P = 8, rank 3, M = N = 4096, K = 512 (the HBM-bound,
 communication-dominant case), rotating buffer sets so the 256 MB
 last-level cache cannot serve the inputs.  The K = 4096 compute-bound case
-(M = N = 32768) is measured in the same run and reported under "secondary".
+(M = N = 32768) is measured in the same run and reported under "secondary"
+(--secondary-all adds the K = 2048 and K = 8192 cases).
+
+roofline.traffic is the fused kernel's measured HBM traffic per launch, read
+from profiles/pmc_traffic.txt (rocprofv3 FETCH_SIZE and WRITE_SIZE, each
+scaled by what the counter reads for a plain device copy of known size, see
+--copy-calibration); it is null when that file was taken from other kernel
+sources than the ones in the tree.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
+    python bench.py --copy-calibration     # 5 device copies of 512 MiB, for the counters
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -42,6 +51,10 @@ def parse():
     p.add_argument("--owned-split", type=int, default=0, choices=(-1, 0, 1),
                    help="owned shard in 64x128 sub-tiles: 1 on, -1 off, 0 library default")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--secondary-all", action="store_true",
+                   help="also measure the K=2048 and K=8192 workloads")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run 5 device copies of 512 MiB (counter calibration) and exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm-only", action="store_true")
     p.add_argument("--sweep", action="store_true",
@@ -137,16 +150,54 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
     return res
 
 
+def source_digest():
+    """sha256 over the HIP sources of the library (the kernel the counters saw)."""
+    d = os.path.join(ROOT, "gemm_reduce_scatter_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_for(w):
+    """Measured HBM bytes per launch of the fused kernel on workload w, or None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    try:
+        with open(path) as f:
+            rec = json.loads(f.read())
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    e = rec.get("workloads", {}).get(w.name)
+    if not e:
+        return None
+    return int(round(e["fetch_kib"] * 1024 * rec["copy_fetch_factor"]
+                     + e["write_kib"] * 1024 * rec["copy_write_factor"]))
+
+
+def copy_calibration(torch):
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "calls": 5}), flush=True)
+
+
 def roofline_of(w, kernel_ms, metrics):
     if w.flops() / w.algorithmic_bytes() > metrics.PEAK_BF16_DENSE_FLOPS / metrics.PEAK_HBM_BYTES:
         ach = w.flops() / (kernel_ms * 1e-3) / 1e12
         peak = metrics.PEAK_BF16_DENSE_FLOPS / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None}
+                "frac": round(ach / peak, 4), "traffic": traffic_for(w)}
     ach = w.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
     peak = metrics.PEAK_HBM_BYTES / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": peak, "unit": "GB/s",
-            "frac": round(ach / peak, 4), "traffic": None}
+            "frac": round(ach / peak, 4), "traffic": traffic_for(w)}
 
 
 def cpu_baseline(w, gen, budget_s=12.0):
@@ -188,8 +239,11 @@ def main():
     from gemm_reduce_scatter_amd import inputs as gen
     from gemm_reduce_scatter_amd import metrics
 
-    pk.load()
     torch.cuda.init()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    pk.load()
     w = gen.WORKLOADS[args.workload]
     if args.sweep:
         w = gen.WORKLOADS["large_k"]
@@ -230,18 +284,29 @@ def main():
     if "gemm_only_kernel_ms" in r:
         line["gemm_only_kernel_ms"] = round(r["gemm_only_kernel_ms"], 5)
         line["exposed_fraction"] = round(r["exposed_fraction"], 4)
-    if not args.no_secondary and args.workload != "compute_bound":
-        w2 = gen.WORKLOADS["compute_bound"]
-        r2 = measure(w2, args.__class__(**{**vars(args), "chunk_rows": None}), torch, gen, pk,
-                     metrics, max(5, args.steps // 5), 3, rotate=False,
-                     gemm_only=not args.no_gemm_only)
-        sec = {"workload": w2.name, "K": w2.K, "M": w2.M, "kernel_ms": round(r2["kernel_ms"], 4),
-               "tflops": round(w2.flops() / (r2["kernel_ms"] * 1e-3) / 1e12, 2),
-               "roofline": roofline_of(w2, r2["kernel_ms"], metrics)}
-        if "gemm_only_kernel_ms" in r2:
-            sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
-            sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
-        line["secondary"] = sec
+    if not args.no_secondary:
+        names = ["compute_bound"]
+        if args.secondary_all:
+            names = ["near_threshold", "compute_bound", "large_k"]
+        secs = []
+        for name in names:
+            if name == args.workload:
+                continue
+            w2 = gen.WORKLOADS[name]
+            r2 = measure(w2, args.__class__(**{**vars(args), "chunk_rows": None,
+                                               "tile_order": None}), torch, gen, pk,
+                         metrics, max(5, args.steps // 5), 3, rotate=False,
+                         gemm_only=not args.no_gemm_only)
+            sec = {"workload": w2.name, "K": w2.K, "M": w2.M, "tile_order": r2["tile_order"],
+                   "chunk_rows": r2["chunk_rows"], "kernel_ms": round(r2["kernel_ms"], 4),
+                   "tflops": round(w2.flops() / (r2["kernel_ms"] * 1e-3) / 1e12, 2),
+                   "roofline": roofline_of(w2, r2["kernel_ms"], metrics)}
+            if "gemm_only_kernel_ms" in r2:
+                sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
+                sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
+            secs.append(sec)
+        if secs:
+            line["secondary"] = secs[0] if len(secs) == 1 else secs
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gen)
     print(json.dumps(line), flush=True)
