@@ -311,28 +311,61 @@ struct Reader {
   }
 };
 
-// One stage of the main loop: MFMA over `cur` (KK k16 steps, fragments of
-// step kk+1 read while step kk multiplies) while a share of the loads of the
-// stage STAGES-1 ahead, into `nxt`, is issued before each step.  A stage past
-// K loads zeros (every lane fails the k bound), so the loop body has no
-// branches, the number of loads in flight is fixed, and the accumulators stay
-// in place across iterations.  The stage ends when this wave's loads of the
-// next stage have landed and every wave has finished reading `cur`.
+// Issue order of one k16 step, for the compiler's scheduler: MFMA i is
+// followed by fragment read i of the next step (while there are any) and
+// load i of the stage ahead (while there are any).  A wave issues in order
+// and a 32x32x16 MFMA holds the issue port for many cycles, so reads and
+// loads placed after the whole MFMA group would start late.
+template <int I, int N, int NR, int NV>
+__device__ __forceinline__ void step_pattern() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+    if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+    step_pattern<I + 1, N, NR, NV>();
+  }
+}
+
+// One stage of the main loop: MFMA over `cur` in KK k16 steps while a share
+// of the loads of the stage STAGES-1 ahead (into `nxt`) is issued before each
+// step.  Fragments run one step ahead: step kk multiplies the fragments read
+// during step kk-1.  The last step first waits for this wave's loads of the
+// next stage, meets the other waves at the barrier (after which every wave
+// has finished reading `cur` and the next stage is complete), reads the
+// next stage's first fragments from `nbuf` and only then multiplies, so the
+// LDS latency at the stage boundary hides behind that step's MFMAs and the
+// barrier behind the previous step's.  A stage past K loads zeros (every
+// lane fails the k bound), so the loop body has no branches, the number of
+// loads in flight is fixed, and the accumulators stay in place across
+// iterations.
 template <class C, int KKI>
 __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
                                             const typename Loader<C>::Stage& ns,
                                             const Reader<C>& rd, const unsigned char* cur,
-                                            unsigned char* nxt, int wave, int rows_valid,
-                                            int col0, f32x16 (&acc)[C::FM][C::FN],
+                                            unsigned char* nxt, const unsigned char* nbuf,
+                                            int wave, int rows_valid, int col0,
+                                            f32x16 (&acc)[C::FM][C::FN],
                                             typename Reader<C>::Frags (&f)[2]) {
   if constexpr (KKI < C::KK) {
     constexpr int QP = (C::LOADS + C::KK - 1) / C::KK;   // loads issued per k16 step
     constexpr int Q0 = KKI * QP < C::LOADS ? KKI * QP : C::LOADS;
     constexpr int Q1 = (KKI + 1) * QP < C::LOADS ? (KKI + 1) * QP : C::LOADS;
     ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
-    if constexpr (KKI + 1 < C::KK) rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
+    if constexpr (KKI + 1 < C::KK) {
+      rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
+    } else {
+      // Every read of `cur` has returned (its fragments feed the MFMAs of
+      // this and the previous step), so the barrier also ends all use of it.
+      wait_vm<(C::STAGES - 2) * C::LOADS>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      rd.read(nbuf, 0, f[(KKI + 1) & 1]);
+    }
     Reader<C>::mfma(f[KKI & 1], acc);
-    stage_steps<C, KKI + 1>(a, ld, ns, rd, cur, nxt, wave, rows_valid, col0, acc, f);
+    step_pattern<0, C::FM * C::FN, C::FM + 2 * C::FN, (KKI + 1 < C::KK) ? Q1 - Q0 : 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    stage_steps<C, KKI + 1>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc, f);
   }
 }
 
@@ -340,19 +373,12 @@ template <class C>
 __device__ __forceinline__ void main_stage(const KArgs& a, const Loader<C>& ld,
                                            const typename Loader<C>::Stage& ns,
                                            const Reader<C>& rd, const unsigned char* cur,
-                                           unsigned char* nxt, int wave, int rows_valid,
-                                           int col0, f32x16 (&acc)[C::FM][C::FN]) {
-  typename Reader<C>::Frags f[2];
-  rd.read(cur, 0, f[0]);
-  stage_steps<C, 0>(a, ld, ns, rd, cur, nxt, wave, rows_valid, col0, acc, f);
-  // This wave's loads of the next stage have landed; every read of `cur` has
-  // returned (its fragments were consumed by the MFMAs above).  A bare
-  // barrier then suffices: a workgroup fence here would also wait for the
-  // loads still in flight for the stages after the next.
-  wait_vm<(C::STAGES - 2) * C::LOADS>();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+                                           unsigned char* nxt, const unsigned char* nbuf,
+                                           int wave, int rows_valid, int col0,
+                                           f32x16 (&acc)[C::FM][C::FN],
+                                           typename Reader<C>::Frags (&f)[2]) {
+  static_assert(C::KK % 2 == 0, "the next stage's first fragments land in f[0]");
+  stage_steps<C, 0>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc, f);
 }
 
 // Stage buffer I of the ring (compile-time, so every LDS access names one
@@ -628,6 +654,8 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+  typename Reader<C>::Frags f[2];
+  if (nk > 0) rd.read(b0, 0, f[0]);
   // Owned sub-items read their peer partials now; the loads must land by the
   // end of the first step, one stage of MFMA later.
   if constexpr (PREF) pf.load(a, lrow0, col0, wm, wn, lane);
@@ -639,8 +667,8 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
     for (int kq = 0; kq < nk; kq += S) {
 #define PK_STEP(I)                                                                           \
   main_stage<C>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,             \
-                pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3), wave,   \
-                rows_valid, col0, acc)
+                pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3),         \
+                pick<((I) + 1) % S>(b0, b1, b2, b3), wave, rows_valid, col0, acc, f)
       PK_STEP(0);
       PK_STEP(1);
       if constexpr (S > 2) PK_STEP(2);
