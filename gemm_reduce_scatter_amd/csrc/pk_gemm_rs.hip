@@ -151,9 +151,13 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// 16-byte store of output data (send chunks, the owned shard, GEMM-only C).
+// 16-byte store of output data (send chunks, the owned shard, GEMM-only C),
+// written through the L2 to memory (sc0 sc1): nothing here reads it back,
+// and a device-scope release then has few dirty lines to write back.  The
+// compiler does not see the store, so the wait states a following write of
+// its data registers needs are issued here.
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -337,26 +341,31 @@ __device__ __forceinline__ void step_pattern() {
 // barrier behind the previous step's.  A stage past K loads zeros (every
 // lane fails the k bound), so the loop body has no branches, the number of
 // loads in flight is fixed, and the accumulators stay in place across
-// iterations.
-template <class C, int KKI>
+// iterations.  `bg` gets one hook per step (step STG*KK + kk of the trip) to
+// issue background loads; it issues BG::LOADS_PER_STEP of them.
+template <class C, int STG, int KKI, class BG>
 __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
                                             const typename Loader<C>::Stage& ns,
                                             const Reader<C>& rd, const unsigned char* cur,
                                             unsigned char* nxt, const unsigned char* nbuf,
                                             int wave, int rows_valid, int col0,
                                             f32x16 (&acc)[C::FM][C::FN],
-                                            typename Reader<C>::Frags (&f)[2]) {
+                                            typename Reader<C>::Frags (&f)[2], BG& bg) {
   if constexpr (KKI < C::KK) {
     constexpr int QP = (C::LOADS + C::KK - 1) / C::KK;   // loads issued per k16 step
     constexpr int Q0 = KKI * QP < C::LOADS ? KKI * QP : C::LOADS;
     constexpr int Q1 = (KKI + 1) * QP < C::LOADS ? (KKI + 1) * QP : C::LOADS;
     ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
+    bg.template step<STG * C::KK + KKI>(a);
     if constexpr (KKI + 1 < C::KK) {
       rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
     } else {
       // Every read of `cur` has returned (its fragments feed the MFMAs of
       // this and the previous step), so the barrier also ends all use of it.
-      wait_vm<(C::STAGES - 2) * C::LOADS>();
+      // Loads complete in issue order; younger than the next stage's are
+      // the two stages after it and the background loads of the last two
+      // stages, which may stay in flight.
+      wait_vm<(C::STAGES - 2) * C::LOADS + 2 * C::KK * BG::LOADS_PER_STEP>();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -365,21 +374,31 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
     Reader<C>::mfma(f[KKI & 1], acc);
     step_pattern<0, C::FM * C::FN, C::FM + 2 * C::FN, (KKI + 1 < C::KK) ? Q1 - Q0 : 0>();
     __builtin_amdgcn_sched_barrier(0);
-    stage_steps<C, KKI + 1>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc, f);
+    stage_steps<C, STG, KKI + 1, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc,
+                                     f, bg);
   }
 }
 
-template <class C>
+template <class C, int STG, class BG>
 __device__ __forceinline__ void main_stage(const KArgs& a, const Loader<C>& ld,
                                            const typename Loader<C>::Stage& ns,
                                            const Reader<C>& rd, const unsigned char* cur,
                                            unsigned char* nxt, const unsigned char* nbuf,
                                            int wave, int rows_valid, int col0,
                                            f32x16 (&acc)[C::FM][C::FN],
-                                           typename Reader<C>::Frags (&f)[2]) {
+                                           typename Reader<C>::Frags (&f)[2], BG& bg) {
   static_assert(C::KK % 2 == 0, "the next stage's first fragments land in f[0]");
-  stage_steps<C, 0>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc, f);
+  stage_steps<C, STG, 0, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc, f, bg);
 }
+
+// No background work.
+struct NoBackground {
+  static constexpr int LOADS_PER_STEP = 0;
+  template <int I>
+  __device__ __forceinline__ void step(const KArgs&) {}
+  __device__ __forceinline__ void end_trip() {}
+  __device__ __forceinline__ void finish(const KArgs&) {}
+};
 
 // Stage buffer I of the ring (compile-time, so every LDS access names one
 // array).
@@ -446,6 +465,34 @@ struct Seg {
   }
 };
 
+// The owned shard's value is (sum_j peer_j) + C: the staged peer partials
+// added in ascending slot order starting from 0, then the local partial.
+// The sum comes from one of three sources, all with that order:
+//  kPeersDirect   - loaded in the epilogue, GS slots at a time;
+//  kPeersPrefetch - every slot of every segment read into registers before
+//                   the item's main loop (GS = P-1);
+//  kPeersPresum   - summed in the background while the workgroup multiplied
+//                   a send tile just before this item (PresumStream).
+enum PeerSource : int { kPeersDirect = 0, kPeersPrefetch = 1, kPeersPresum = 2 };
+
+__device__ __forceinline__ void add_bf16x8(float (&t)[8], u32x4 v) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    t[2 * p] += bf16lo(v[p]);
+    t[2 * p + 1] += bf16hi(v[p]);
+  }
+}
+
+// As add_bf16x8 when `ok`, else adds +0 (the sums start at +0 and never
+// hold -0, so this leaves them unchanged).
+__device__ __forceinline__ void add_bf16x8_if(float (&t)[8], u32x4 v, bool ok) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    t[2 * p] += ok ? bf16lo(v[p]) : 0.0f;
+    t[2 * p + 1] += ok ? bf16hi(v[p]) : 0.0f;
+  }
+}
+
 // Peer partials of every segment of an owned item, read into registers
 // before the main loop so the loads overlap it (GS = P-1 slots).
 template <class C, int GS>
@@ -471,8 +518,77 @@ struct PeerPrefetch {
   }
 };
 
-template <int GS>
-struct NoPrefetch {};
+// The peer sum of an owned sub-tile (configuration CO, GS = P-1 slots),
+// accumulated by a workgroup while it multiplies a send tile whose main loop
+// has STEPS k16 steps per trip.  Load g (g = trip*STEPS + step) reads slot
+// g/SEGS of segment g%SEGS; each segment keeps one load in flight and adds
+// it when it issues its next one, SEGS steps later.  The loads go through a
+// buffer descriptor over the peer partials: slots past P-2 get an offset
+// past its range and read zeros, which add nothing (the sums start at +0
+// and never hold -0).  finish() adds the last loads and any slots a short K
+// left unread.  Byte offsets are 32-bit: the owned split requires the peer
+// partials to span less than 2^31 bytes.
+template <class CO, int GS, int STEPS>
+struct PresumStream {
+  using SG = Seg<CO>;
+  static constexpr int SEGS = SG::COUNT;
+  static constexpr int SPT = STEPS / SEGS;              // slots per trip
+  static constexpr int LOADS_PER_STEP = 1;
+  static_assert(STEPS % SEGS == 0, "whole segments per trip");
+  float v[SEGS][8];
+  u32x4 q[SEGS];
+  uint32_t off[SEGS];          // byte offset of each segment in slot 0
+  uint32_t slot_bytes;
+  __amdgpu_buffer_rsrc_t rsrc;
+  int trip;
+
+  __device__ __forceinline__ void init(const KArgs& a, int lrow0, int col0, int wm, int wn,
+                                       int lane) {
+    rsrc = make_rsrc(a.peers);
+    slot_bytes = (uint32_t)a.S * (uint32_t)a.N * 2u;
+    const int col = col0 + SG::col(wn, lane);
+#pragma unroll
+    for (int fm = 0; fm < CO::FM; ++fm)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int it = 0; it < SG::PASSES; ++it) {
+          const int lr = lrow0 + SG::row(wm, lane, fm, h, it);
+          const bool ok = lr < a.S && col < a.N;
+          const int sg = (fm * 2 + h) * SG::PASSES + it;
+          off[sg] = ok ? ((uint32_t)lr * (uint32_t)a.N + (uint32_t)col) * 2u : 0u;   // row 0 stays in bounds
+        }
+#pragma unroll
+    for (int sg = 0; sg < SEGS; ++sg) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[sg][e] = 0.0f;
+      q[sg] = u32x4{0u, 0u, 0u, 0u};
+    }
+    trip = 0;
+  }
+
+  __device__ __forceinline__ u32x4 load(uint32_t off_b, int slot) const {
+    const uint32_t o = slot < GS ? off_b + (uint32_t)slot * slot_bytes : kOffNone;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, 0));
+  }
+
+  template <int I>
+  __device__ __forceinline__ void step(const KArgs&) {
+    constexpr int sg = I % SEGS, so = I / SEGS;
+    add_bf16x8(v[sg], q[sg]);                            // the previous slot, or zeros
+    q[sg] = load(off[sg], trip * SPT + so);
+  }
+  __device__ __forceinline__ void end_trip() { ++trip; }
+  __device__ __forceinline__ void finish(const KArgs&) {
+#pragma unroll
+    for (int sg = 0; sg < SEGS; ++sg) add_bf16x8(v[sg], q[sg]);
+    for (int slot = trip * SPT; slot < GS; ++slot)
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg) add_bf16x8(v[sg], load(off[sg], slot));
+  }
+};
+
+struct NoPeers {};
 
 __device__ __forceinline__ void store_out(const KArgs& a, long long base, const float (&s)[8]) {
   if (a.out_bf16) {
@@ -488,17 +604,17 @@ __device__ __forceinline__ void store_out(const KArgs& a, long long base, const 
   }
 }
 
-template <class C, int MODE, int GS, class PF>
+template <class C, int MODE, int GS, int SRC, class PV>
 __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, int col0,
                                          float* lds_f, int wave, int wm, int wn, int lane,
-                                         f32x16 (&acc)[C::FM][C::FN], const PF& pf) {
+                                         f32x16 (&acc)[C::FM][C::FN], const PV& pv) {
   using SG = Seg<C>;
-  constexpr bool PREF = !__is_same(PF, NoPrefetch<GS>);
   float* stage = lds_f + wave * 16 * C::EPI_STRIDE;
   constexpr int LPR = SG::LPR, RPI = SG::RPI, PASSES = SG::PASSES;
   // owned segments summed together: 4 for small wave tiles, 2 when the
   // accumulators take a large part of the register file
-  constexpr int BATCH = PREF ? PASSES : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
+  constexpr int BATCH =
+      SRC != kPeersDirect ? PASSES : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
   static_assert(PASSES % BATCH == 0, "batches tile the passes");
   const bool owned = MODE == kFused && shard == a.rank;
   const int c8 = lane % LPR;
@@ -540,56 +656,49 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
       } else {
 #pragma unroll
         for (int it0 = 0; it0 < PASSES; it0 += BATCH) {
-          float s[BATCH][8];
+          float t[BATCH][8];     // peer sums
           bool ok[BATCH];
           long long base[BATCH];
+#pragma unroll
+          for (int b = 0; b < BATCH; ++b) {
+            const int lr = lrow0 + SG::row(wm, lane, fm, h, it0 + b);
+            ok[b] = lr < a.S && col_ok;
+            base[b] = ok[b] ? (long long)lr * a.N + col : 0;   // row 0 stays in bounds
+            const int sg = (fm * 2 + h) * PASSES + it0 + b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if constexpr (SRC == kPeersPresum) t[b][e] = pv.v[sg][e];
+              else t[b][e] = 0.0f;
+            }
+            if constexpr (SRC == kPeersPrefetch) {
+#pragma unroll
+              for (int jj = 0; jj < GS; ++jj) add_bf16x8(t[b], pv.v[sg][jj]);
+            }
+          }
+          if constexpr (SRC == kPeersDirect) {
+            // ascending slot order; GS slots' loads are in flight together
+            for (int j0 = 0; j0 < a.P - 1; j0 += GS) {
+              u32x4 q[BATCH][GS];
+#pragma unroll
+              for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+                for (int jj = 0; jj < GS; ++jj)
+                  q[b][jj] = load16(a.peers + (j0 + jj) * slot_stride + base[b]);
+#pragma unroll
+              for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+                for (int jj = 0; jj < GS; ++jj) add_bf16x8(t[b], q[b][jj]);
+            }
+          }
 #pragma unroll
           for (int b = 0; b < BATCH; ++b) {
             const int rr = (it0 + b) * RPI + lane / LPR;
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
-            s[b][0] = x0[0]; s[b][1] = x0[1]; s[b][2] = x0[2]; s[b][3] = x0[3];
-            s[b][4] = x1[0]; s[b][5] = x1[1]; s[b][6] = x1[2]; s[b][7] = x1[3];
-            const int lr = lrow0 + SG::row(wm, lane, fm, h, it0 + b);
-            ok[b] = lr < a.S && col_ok;
-            base[b] = ok[b] ? (long long)lr * a.N + col : 0;   // row 0 stays in bounds
+            float s8[8] = {t[b][0] + x0[0], t[b][1] + x0[1], t[b][2] + x0[2], t[b][3] + x0[3],
+                           t[b][4] + x1[0], t[b][5] + x1[1], t[b][6] + x1[2], t[b][7] + x1[3]};
+            if (ok[b]) store_out(a, base[b], s8);
           }
-          if constexpr (PREF) {
-            // slots 0 .. GS-1 = all P-1 peers, in ascending order
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b) {
-              const int sg = (fm * 2 + h) * PASSES + it0 + b;
-#pragma unroll
-              for (int jj = 0; jj < GS; ++jj)
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                  s[b][2 * p] += bf16lo(pf.v[sg][jj][p]);
-                  s[b][2 * p + 1] += bf16hi(pf.v[sg][jj][p]);
-                }
-            }
-          } else {
-            // ascending slot order; GS slots' loads are in flight together
-            for (int j0 = 0; j0 < a.P - 1; j0 += GS) {
-              u32x4 pv[BATCH][GS];
-#pragma unroll
-              for (int b = 0; b < BATCH; ++b)
-#pragma unroll
-                for (int jj = 0; jj < GS; ++jj)
-                  pv[b][jj] = load16(a.peers + (j0 + jj) * slot_stride + base[b]);
-#pragma unroll
-              for (int b = 0; b < BATCH; ++b)
-#pragma unroll
-                for (int jj = 0; jj < GS; ++jj)
-#pragma unroll
-                  for (int p = 0; p < 4; ++p) {
-                    s[b][2 * p] += bf16lo(pv[b][jj][p]);
-                    s[b][2 * p + 1] += bf16hi(pv[b][jj][p]);
-                  }
-            }
-          }
-#pragma unroll
-          for (int b = 0; b < BATCH; ++b)
-            if (ok[b]) store_out(a, base[b], s[b]);
         }
       }
       wave_lds_sync();
@@ -611,11 +720,14 @@ struct LdsPlan {
 };
 
 // One work item: a tile of configuration C whose first row is shard-local
-// row `lrow0` of shard `shard` and whose first column is `col0`.
-template <class C, int MODE, int GS, bool PREF>
+// row `lrow0` of shard `shard` and whose first column is `col0`.  `bg` runs
+// in the background of the main loop; an owned item takes its peer sum from
+// source SRC (`pv` for kPeersPresum).
+template <class C, int MODE, int GS, int SRC, class BG, class PV>
 __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, int col0,
                                         unsigned char* b0, unsigned char* b1, unsigned char* b2,
-                                        unsigned char* b3, int tid, int wave, int lane) {
+                                        unsigned char* b3, int tid, int wave, int lane, BG& bg,
+                                        const PV& pv) {
   constexpr int S = C::STAGES;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   Loader<C> ld;
@@ -644,7 +756,7 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
       ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave, rows_valid,
                                col0);
   }
-  using PFT = typename std::conditional<PREF, PeerPrefetch<C, GS>, NoPrefetch<GS>>::type;
+  using PFT = typename std::conditional<SRC == kPeersPrefetch, PeerPrefetch<C, GS>, NoPeers>::type;
   PFT pf;
   if (nk > 0) {
     // Loads complete in issue order, so this leaves stages 1 .. S-2 in
@@ -658,7 +770,7 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   if (nk > 0) rd.read(b0, 0, f[0]);
   // Owned sub-items read their peer partials now; the loads must land by the
   // end of the first step, one stage of MFMA later.
-  if constexpr (PREF) pf.load(a, lrow0, col0, wm, wn, lane);
+  if constexpr (SRC == kPeersPrefetch) pf.load(a, lrow0, col0, wm, wn, lane);
   if (nk > 0) {
     // S steps per trip, step I multiplies buffer I and fills buffer
     // (I + S - 1) % S with the stage S-1 ahead.  A last partial trip
@@ -666,26 +778,36 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
     // (they never hold -0).
     for (int kq = 0; kq < nk; kq += S) {
 #define PK_STEP(I)                                                                           \
-  main_stage<C>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,             \
-                pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3),         \
-                pick<((I) + 1) % S>(b0, b1, b2, b3), wave, rows_valid, col0, acc, f)
+  main_stage<C, (I), BG>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,     \
+                         pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3), \
+                         pick<((I) + 1) % S>(b0, b1, b2, b3), wave, rows_valid, col0, acc, f, bg)
       PK_STEP(0);
       PK_STEP(1);
       if constexpr (S > 2) PK_STEP(2);
       if constexpr (S > 3) PK_STEP(3);
 #undef PK_STEP
+      bg.end_trip();
     }
     wait_vm0();        // loads of stages past the end (zeros) into the staging area
     __syncthreads();
   }
+  bg.finish(a);
 
-  epilogue<C, MODE, GS, PFT>(a, shard, lrow0, col0, reinterpret_cast<float*>(b0), wave, wm, wn,
-                             lane, acc, pf);
+  using PVT = typename std::conditional<SRC == kPeersPrefetch, PFT, PV>::type;
+  const PVT* src;
+  if constexpr (SRC == kPeersPrefetch) src = &pf;
+  else src = &pv;
+  epilogue<C, MODE, GS, SRC, PVT>(a, shard, lrow0, col0, reinterpret_cast<float*>(b0), wave, wm,
+                                  wn, lane, acc, *src);
 }
 
 // The persistent kernel: workgroup w takes walk positions w, w+G, w+2G, ...
-// Whole tiles use configuration CS; owned sub-tiles (owned split R > 1) use
-// the smaller CO, with the peer partials read ahead into registers.
+// Whole tiles use configuration CS.  Under the owned split (CO != CS) a
+// position holds a send tile and an owned CO sub-tile: the workgroup
+// multiplies the send tile while it sums the sub-tile's peer partials in the
+// background, sends, then multiplies the sub-tile and adds that sum.
+// Positions past the end of one list hold only the other (a lone sub-tile
+// reads its peer partials ahead into registers).
 template <class CS, class CO, int MODE, int GS>
 __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   using L = LdsPlan<CS, CO>;
@@ -706,23 +828,49 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
 
+  NoBackground nobg;
+  NoPeers nopv;
   // Finished send tiles are signalled in batches: one device-scope release
   // (an L2 writeback on this multi-XCD part, several microseconds) covers up
   // to a.sig_batch tiles.  Positions fs, fs+G, ..., up to the current one
   // hold the tiles not yet signalled.
   long long fs = w;
   int npend = 0;
+  const long long n_send = SPLIT ? split_sends(a.g) : 0;
+  const long long n_own = SPLIT ? split_owned(a.g) : 0;
   for (long long s = w; s < a.total_tiles; s += G) {
-    const TileCoord tc = tile_at(a.g, s);
-    if (!SPLIT || tc.sub < 0) {
-      process<CS, MODE, GS, false>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1, lds2,
-                                   lds3, tid, wave, lane);
+    if constexpr (!SPLIT) {
+      const TileCoord tc = tile_at(a.g, s);
+      process<CS, MODE, GS, kPeersDirect>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1,
+                                          lds2, lds3, tid, wave, lane, nobg, nopv);
       if (MODE == kFused && tc.shard != a.rank) ++npend;
-    } else if constexpr (SPLIT) {
-      const int sm = tc.sub / a.g.Rn, sn = tc.sub - sm * a.g.Rn;
-      process<CO, MODE, GS, true>(a, tc.shard, tc.t * CS::BM + sm * CO::BM,
-                                  tc.u * CS::BN + sn * CO::BN, lds0, lds1, lds2, lds3, tid, wave,
-                                  lane);
+    } else {
+      const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
+      if (s < n_send) {
+        const TileCoord st = send_item(a.g, s);
+        if (s < n_own) {
+          const TileCoord ot = owned_item(a.g, s);
+          const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+          const int olr = ot.t * CS::BM + sm * CO::BM, oc = ot.u * CS::BN + sn * CO::BN;
+          PresumStream<CO, GS, CS::STAGES * CS::KK> ps;
+          ps.init(a, olr, oc, wm, wn, lane);
+          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+                                              lds1, lds2, lds3, tid, wave, lane, ps, nopv);
+          __syncthreads();   // the staging area is the sub-tile's first stage
+          process<CO, MODE, GS, kPeersPresum>(a, ot.shard, olr, oc, lds0, lds1, lds2, lds3, tid,
+                                              wave, lane, nobg, ps);
+        } else {
+          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+                                              lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
+        }
+        ++npend;
+      } else {
+        const TileCoord ot = owned_item(a.g, s);
+        const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+        process<CO, MODE, GS, kPeersPrefetch>(a, ot.shard, ot.t * CS::BM + sm * CO::BM,
+                                              ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
+                                              lds3, tid, wave, lane, nobg, nopv);
+      }
     }
     if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || s + G >= a.total_tiles)) {
       wait_vm0();            // this thread's stores have reached the cache
@@ -730,8 +878,12 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
         for (long long s2 = fs; s2 <= s; s2 += G) {
-          const TileCoord t2 = tile_at(a.g, s2);
-          if (t2.shard != a.rank) signal_chunks(a, t2, CS::BM);
+          if constexpr (SPLIT) {
+            if (s2 < n_send) signal_chunks(a, send_item(a.g, s2), CS::BM);
+          } else {
+            const TileCoord t2 = tile_at(a.g, s2);
+            if (t2.shard != a.rank) signal_chunks(a, t2, CS::BM);
+          }
         }
       }
       fs = s + G;
@@ -865,10 +1017,13 @@ static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
 // Owned split of configuration `cfg` for a call: on request, or by default
 // when the whole-tile walk gives fewer than two tiles per CU (the owned
 // tiles then sit on the critical path).  Available for configuration 1 with
-// P - 1 in {1, 3, 7} (all peer slots are read ahead in one batch).
-static bool use_owned_split(int cfg, int P, long long whole_tiles, const pk_options* o) {
+// P - 1 in {1, 3, 7} (all peer slots of a segment in one batch) and peer
+// partials spanning less than 2^31 bytes (32-bit buffer offsets).
+static bool use_owned_split(int cfg, int P, long long S, long long N, long long whole_tiles,
+                            const pk_options* o) {
   const int req = o ? o->owned_split : 0;
-  const bool able = cfg == 1 && (P == 2 || P == 4 || P == 8);
+  const bool able = cfg == 1 && (P == 2 || P == 4 || P == 8) &&
+                    2LL * (P - 1) * S * N < (1LL << 31) - 16;
   if (req < 0 || !able) return false;
   if (req > 0) return true;
   return whole_tiles < 2LL * kAssumedCUs;
@@ -882,12 +1037,12 @@ static int launch(KArgs& a, bool gemm_only, int cfg, const pk_options* o, hipStr
   a.g.Tn = ceil_div(a.N, C::BN);
   a.g.group_n = (o && o->group_n > 0) ? o->group_n : default_group_n(kCfgs[0], a.g.Tn);
   a.g.Rm = a.g.Rn = 1;
-  const bool split = !gemm_only && use_owned_split(cfg, a.P, a.g.total(), o);
+  const bool split = !gemm_only && use_owned_split(cfg, a.P, a.S, a.N, a.g.total(), o);
   if (split) {
     a.g.Rm = C::BM / CfgOwned::BM;
     a.g.Rn = C::BN / CfgOwned::BN;
   }
-  a.total_tiles = a.g.total();
+  a.total_tiles = split ? split_pairs(a.g) : a.g.total();
   if (a.total_tiles == 0) return PK_OK;
   if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
   if constexpr (__is_same(C, Cfg1)) {
@@ -1045,12 +1200,25 @@ int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile
   g.Rm = owned_split ? pk::Cfg1::BM / pk::CfgOwned::BM : 1;
   g.Rn = owned_split ? pk::Cfg1::BN / pk::CfgOwned::BN : 1;
   const long long total = g.total();
-  for (long long s = 0; s < total && s < cap; ++s) {
-    const pk::TileCoord tc = pk::tile_at(g, s);
-    out4[4 * s] = tc.shard;
-    out4[4 * s + 1] = tc.t;
-    out4[4 * s + 2] = tc.u;
-    out4[4 * s + 3] = tc.sub;
+  long long n = 0;
+  auto put = [&](const pk::TileCoord& tc) {
+    if (n < cap) {
+      out4[4 * n] = tc.shard;
+      out4[4 * n + 1] = tc.t;
+      out4[4 * n + 2] = tc.u;
+      out4[4 * n + 3] = tc.sub;
+    }
+    ++n;
+  };
+  if (!owned_split) {
+    for (long long s = 0; s < total; ++s) put(pk::tile_at(g, s));
+  } else {
+    // pairs in walk order: the send tile, then its owned sub-tile
+    const long long pairs = pk::split_pairs(g);
+    for (long long s = 0; s < pairs; ++s) {
+      if (s < pk::split_sends(g)) put(pk::send_item(g, s));
+      if (s < pk::split_owned(g)) put(pk::owned_item(g, s));
+    }
   }
   return total;
 }

@@ -21,18 +21,23 @@
 // (BN/Rn), each its own work item, so that the heavy owned epilogue (it
 // reads P-1 staged partials per element) is spread over many workgroups
 // instead of falling on the few that hold whole owned tiles.  R = 1 keeps
-// whole tiles.
+// whole tiles.  Under the split the walk is a list of pairs: position s
+// holds send tile s (in the tile order, owned shard skipped) and owned
+// sub-tile s (in the owned shard's own order), either of which may be
+// missing past the end of its list; the workgroup that runs the pair reads
+// the sub-tile's peer partials while it multiplies the send tile.
 //
 // Tile orders (the order work items are handed out; results never depend on
 // it, Syncopate section 5.2 "Tile-Scheduler Swizzling" reorders waves the same
 // way without moving data):
 //   0 row-major:        shards 0 .. P-1, each shard chunk-major;
 //   1 owned-first:      shards rank, rank+1, ..., rank+P-1 (mod P);
-//   2 dest-round-robin: round i holds tile i of shards rank+1, ...,
-//                       rank+P-1 (one per destination) followed by the R
-//                       items of owned tile i, so consecutive tiles go to
-//                       different destinations and the owned shard comes
-//                       last in every round.
+//   2 dest-round-robin: position s takes tile s/P of shard (rank+1+s) mod P,
+//                       so consecutive tiles go to different destinations
+//                       and the owned shard comes last in every round.
+// Under the owned split the order applies to the send tiles (owned-first
+// then lists shards rank+1, ..., rank+P-1, each owned sub-tile riding with
+// its send tile).
 #pragma once
 #include <stdint.h>
 
@@ -79,43 +84,64 @@ PK_HD void intra_shard(const Grid& g, long long i, int& t, int& u) {
   u = u0 + (int)(r - (long long)t * width);
 }
 
-// Work item at walk position s (0 <= s < total()).
+// Whole tile at walk position s (0 <= s < P*Tm*Tn) when there is no owned
+// split.
 PK_HD TileCoord tile_at(const Grid& g, long long s) {
   TileCoord c;
   const long long per = g.tiles_per_shard();
-  const int R = g.R();
-  long long i;       // tile index inside its shard
-  int sub = -1;      // owned sub-tile
+  long long i;
   if (g.order == kDestRoundRobin) {
-    const long long L = g.P - 1 + R;                      // items per round
-    i = s / L;
-    const int j = (int)(s - i * L);
-    if (j < g.P - 1) {
-      c.shard = (g.rank + 1 + j) % g.P;
-    } else {
-      c.shard = g.rank;
-      sub = j - (g.P - 1);
-    }
+    c.shard = (int)((g.rank + 1 + s % g.P) % g.P);
+    i = s / g.P;
+  } else if (g.order == kOwnedFirst) {
+    c.shard = (int)((g.rank + s / per) % g.P);
+    i = s % per;
   } else {
-    // shards in walk order; the owned one takes R * per positions
-    const int first = g.order == kOwnedFirst ? g.rank : 0;
-    const long long own_start =
-        g.order == kOwnedFirst ? 0 : (long long)g.rank * per;   // positions before the owned block
-    if (s >= own_start && s < own_start + R * per) {
-      c.shard = g.rank;
-      const long long q = s - own_start;
-      i = q / R;
-      sub = (int)(q - i * R);
-    } else {
-      const long long q = s < own_start ? s : s - (long long)(R - 1) * per;
-      const int k = (int)(q / per);                           // k-th shard in walk order
-      c.shard = (first + k) % g.P;
-      i = q - (long long)k * per;
-    }
+    c.shard = (int)(s / per);
+    i = s % per;
   }
   intra_shard(g, i, c.t, c.u);
-  c.sub = (c.shard == g.rank && R > 1) ? sub : -1;
+  c.sub = -1;
   return c;
+}
+
+// Owned sub-tile j of the owned shard under the split (0 <= j < R*Tm*Tn).
+PK_HD TileCoord owned_item(const Grid& g, long long j) {
+  TileCoord c;
+  const int R = g.R();
+  const long long i = j / R;
+  c.shard = g.rank;
+  c.sub = (int)(j - i * R);
+  intra_shard(g, i, c.t, c.u);
+  return c;
+}
+
+// Send tile i (0 <= i < (P-1)*Tm*Tn) in the tile order, the owned shard
+// skipped.
+PK_HD TileCoord send_item(const Grid& g, long long i) {
+  TileCoord c;
+  const long long per = g.tiles_per_shard();
+  long long k, r;
+  if (g.order == kDestRoundRobin) {
+    k = i % (g.P - 1);
+    r = i / (g.P - 1);
+    c.shard = (int)((g.rank + 1 + k) % g.P);
+  } else {
+    k = i / per;
+    r = i - k * per;
+    if (g.order == kOwnedFirst) c.shard = (int)((g.rank + 1 + k) % g.P);
+    else c.shard = k < g.rank ? (int)k : (int)k + 1;
+  }
+  c.sub = -1;
+  intra_shard(g, r, c.t, c.u);
+  return c;
+}
+
+// Under the split: the pair at walk position s (0 <= s < pairs()).
+PK_HD long long split_sends(const Grid& g) { return g.tiles_per_shard() * (g.P - 1); }
+PK_HD long long split_owned(const Grid& g) { return g.tiles_per_shard() * g.R(); }
+PK_HD long long split_pairs(const Grid& g) {
+  return split_sends(g) > split_owned(g) ? split_sends(g) : split_owned(g);
 }
 
 // Send slot of destination d (d != rank): ranks in ascending order, skipping

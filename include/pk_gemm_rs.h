@@ -131,11 +131,13 @@ int pk_config_info(int id, int* BM, int* BN, int* BK, int* WM, int* WN, int* thr
 int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
 
 /* Host copy of the work walk (host only): writes, for each of the first
- * min(cap, total) positions, (shard, row tile, column tile, sub-tile) into
- * out4[4*i .. 4*i+3]; sub-tile is -1 for a whole tile and 0..R-1 for the R
- * sub-tiles of an owned tile under the owned split (owned_split = 1; only
- * configuration 1).  Returns the total number of work items or a negative
- * code.  group_n as in pk_options (0 = auto for this config). */
+ * min(cap, total) work items in the order they are handed out, (shard, row
+ * tile, column tile, sub-tile) into out4[4*i .. 4*i+3]; sub-tile is -1 for a
+ * whole tile and 0..R-1 for the R sub-tiles of an owned tile under the owned
+ * split (owned_split = 1; only configuration 1), where the walk is a list of
+ * pairs, each send tile followed by the owned sub-tile that rides with it.
+ * Returns the total number of work items or a negative code.  group_n as in
+ * pk_options (0 = auto for this config). */
 int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,
                      int group_n, int owned_split, int32_t* out4, int64_t cap);
 

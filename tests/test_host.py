@@ -180,26 +180,34 @@ def test_owned_split_walk_covers_every_item_once(order, shape):
     assert set(keys) == want
 
 
-def test_owned_split_orders():
+def test_owned_split_walk_pairs_send_tiles_with_owned_sub_tiles():
+    """Under the split the walk is a list of pairs: send tile s (tile order,
+    owned shard skipped) followed by owned sub-tile s (owned order)."""
     M, N, P, rank = 4096, 4096, 8, 3
     Tm, Tn = _tiles(M, N, P, 1)
     per = Tm * Tn
-    rm = pk.pk_tile_walk(M, N, P, rank, 1, 0, owned_split=1)
-    shards = list(rm[:, 0])
-    # row-major: shards in order, the owned block R times as long
-    expect = [d for d in range(P) for _ in range(per * (OWNED_R if d == rank else 1))]
-    assert shards == expect
-    own = rm[rank * per:rank * per + OWNED_R * per]
-    assert list(own[:OWNED_R, 3]) == list(range(OWNED_R))           # sub-tiles of one tile together
-    assert len({tuple(x) for x in own[:OWNED_R, 1:3]}) == 1
-    of = pk.pk_tile_walk(M, N, P, rank, 1, 1, owned_split=1)
-    assert set(of[:OWNED_R * per, 0]) == {rank}
+    whole = {o: pk.pk_tile_walk(M, N, P, rank, 1, o) for o in (0, 1, 2)}
+    for order in (0, 1, 2):
+        w = pk.pk_tile_walk(M, N, P, rank, 1, order, owned_split=1)
+        sends = w[w[:, 3] < 0]
+        owned = w[w[:, 3] >= 0]
+        # send tiles keep the whole-tile order with the owned shard removed
+        ref = whole[order][whole[order][:, 0] != rank]
+        if order == 1:       # owned-first lists rank+1, ..., rank+P-1
+            assert list(sends[::per, 0]) == [(rank + 1 + k) % P for k in range(P - 1)]
+        else:
+            assert np.array_equal(sends[:, :3], ref[:, :3])
+        # owned sub-tiles: owned tile j // R, sub-tile j % R, in the owned shard's order
+        own_ref = whole[0][whole[0][:, 0] == rank]
+        assert list(owned[:, 3]) == [j % OWNED_R for j in range(OWNED_R * per)]
+        assert np.array_equal(owned[:, 1:3], np.repeat(own_ref[:, 1:3], OWNED_R, axis=0))
+        # pairing: item 2s is send tile s, item 2s+1 its owned sub-tile
+        n_pairs = min(len(sends), len(owned))
+        assert np.array_equal(w[0:2 * n_pairs:2], sends[:n_pairs])
+        assert np.array_equal(w[1:2 * n_pairs:2], owned[:n_pairs])
     rr = pk.pk_tile_walk(M, N, P, rank, 1, 2, owned_split=1)
-    L = P - 1 + OWNED_R
-    for i in range(3):                                               # round i
-        rnd = rr[i * L:(i + 1) * L]
-        assert list(rnd[:P - 1, 0]) == [(rank + 1 + j) % P for j in range(P - 1)]
-        assert set(rnd[P - 1:, 0]) == {rank} and list(rnd[P - 1:, 3]) == list(range(OWNED_R))
+    s_rr = rr[rr[:, 3] < 0]
+    assert list(s_rr[:P - 1, 0]) == [(rank + 1 + j) % P for j in range(P - 1)]
     with pytest.raises(pk.PkError):
         pk.pk_tile_walk(M, N, P, rank, 2, 0, owned_split=1)          # configuration 1 only
 
