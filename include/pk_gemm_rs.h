@@ -16,8 +16,9 @@
  *       tile of the chunk is stored (the pages' signal primitive; chunks as
  *       in "Syncopate: Efficient Multi-GPU AI Kernels via Automatic Chunk-
  *       Centric Compute-Communication Overlap", section 5.1);
- *   out <- C_loc rows of shard `rank` + sum_j peer_partials[j]   (fp32 adds,
- *       j ascending), stored once.
+ *   out <- sum_j peer_partials[j] + C_loc rows of shard `rank`   (fp32: the
+ *       peers added in ascending slot order starting from +0, then the
+ *       local partial), stored once.
  *
  * The peers' partials are already staged in device memory (what the other
  * ranks sent to this one); nothing here talks to another GPU.
