@@ -127,10 +127,37 @@ def _check_tensors(A, B, peer_partials, send_bufs, out, flags):
         raise ValueError("flags must be a 32-bit integer tensor")
 
 
+def _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
+                 out_bf16, gemm_only=False):
+    """Reject buffers smaller than the kernel reads or writes for these sizes.
+
+    The library sees plain pointers and cannot check this itself.  Argument
+    errors it does detect (M not a multiple of P, bad chunk_rows, ...) are left
+    to it, so this check only runs on sizes it would accept.
+    """
+    M, N, K, P = int(M), int(N), int(K), int(P)
+    if P < 1 or M < 0 or N < 0 or K < 0 or M % P:
+        return
+    S = M // P
+    need = [("A", A, 2 * M * K), ("B", B, 2 * K * N),
+            ("out", out, 2 * M * N if gemm_only else (2 if out_bf16 else 4) * S * N)]
+    if not gemm_only:
+        need += [("peer_partials", peer_partials, 2 * (P - 1) * S * N),
+                 ("send_bufs", send_bufs, 2 * (P - 1) * S * N)]
+        words = load().pk_flags_words(P, M, int(chunk_rows))
+        if words >= 0:
+            need.append(("flags", flags, 4 * words))
+    for name, t, nbytes in need:
+        if t is not None and t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, "
+                             f"the call needs {nbytes}")
+
+
 def pk_gemm_rs_local(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                      chunk_rows, tile_order, stream=None) -> int:
     """Fused share with a float32 ``out``; asynchronous on ``stream``."""
     _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+    _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows, 0)
     return _check(load().pk_gemm_rs_local(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
         int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
@@ -141,6 +168,7 @@ def pk_gemm_rs_local_bf16out(A, B, peer_partials, send_bufs, out, flags, M, N, K
                              chunk_rows, tile_order, stream=None) -> int:
     """Fused share with a bf16 ``out``; asynchronous on ``stream``."""
     _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+    _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows, 1)
     return _check(load().pk_gemm_rs_local_bf16out(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
         int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
@@ -153,6 +181,8 @@ def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, 
                         stream=None) -> int:
     """Fused share with explicit tile configuration / grid / grouping options."""
     _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+    _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows, out_bf16,
+                 gemm_only)
     o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
     return _check(load().pk_gemm_rs_local_ex(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),

@@ -91,6 +91,30 @@ def test_validate_rejects(kw, code):
     assert _v(**kw) == code
 
 
+def test_binding_rejects_short_buffers():
+    """The binding refuses buffers smaller than a call reads or writes."""
+    import torch
+    M, N, K, P, cr = 512, 256, 64, 4, 64
+    S = M // P
+    bf = torch.bfloat16
+
+    def bufs(out_rows, out_dtype=bf, peers_rows=S):
+        return (torch.empty(M, K, dtype=bf), torch.empty(K, N, dtype=bf),
+                torch.empty(P - 1, peers_rows, N, dtype=bf), torch.empty(P - 1, S, N, dtype=bf),
+                torch.empty(out_rows, N, dtype=out_dtype),
+                torch.zeros(pk.pk_flags_words(P, M, cr), dtype=torch.int32))
+
+    pk._check_sizes(*bufs(S), M, N, K, P, cr, 1)
+    pk._check_sizes(*bufs(S, torch.float32), M, N, K, P, cr, 0)
+    pk._check_sizes(*bufs(M), M, N, K, P, cr, 1, gemm_only=True)
+    with pytest.raises(ValueError, match="out"):
+        pk._check_sizes(*bufs(S), M, N, K, P, cr, 1, gemm_only=True)   # gemm-only writes M rows
+    with pytest.raises(ValueError, match="out"):
+        pk._check_sizes(*bufs(S), M, N, K, P, cr, 0)                   # fp32 out in a bf16 buffer
+    with pytest.raises(ValueError, match="peer_partials"):
+        pk._check_sizes(*bufs(S, peers_rows=S - 1), M, N, K, P, cr, 1)
+
+
 def test_config_table():
     n = pk.pk_config_count()
     assert n >= 3
