@@ -136,8 +136,8 @@ def _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_r
     to it, so this check only runs on sizes it would accept.
     """
     M, N, K, P = int(M), int(N), int(K), int(P)
-    if P < 1 or M < 0 or N < 0 or K < 0 or M % P:
-        return
+    if P < 1 or M <= 0 or N <= 0 or K < 0 or M % P:
+        return                    # rejected by the library, or a no-op touching no buffer
     S = M // P
     need = [("A", A, 2 * M * K), ("B", B, 2 * K * N),
             ("out", out, 2 * M * N if gemm_only else (2 if out_bf16 else 4) * S * N)]

@@ -828,17 +828,25 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   int w = blockIdx.x;
   if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
 
+  // Round k covers walk positions kG .. kG+G-1.  Without the split the
+  // position a workgroup takes moves by one every round, so work that recurs
+  // at a fixed stride of the walk (the owned tiles of the round-robin order,
+  // one in every P positions) rotates over the workgroups instead of falling
+  // on the same G/P of them; an XCD's positions in a round stay contiguous.
+  const auto pos = [&](long long k) -> long long {
+    return k * G + (SPLIT ? w : (int)((w + k) % G));
+  };
+
   NoBackground nobg;
   NoPeers nopv;
   // Finished send tiles are signalled in batches: one device-scope release
   // (an L2 writeback on this multi-XCD part, several microseconds) covers up
-  // to a.sig_batch tiles.  Positions fs, fs+G, ..., up to the current one
-  // hold the tiles not yet signalled.
-  long long fs = w;
+  // to a.sig_batch tiles.  Rounds fk .. k hold the tiles not yet signalled.
+  long long fk = 0;
   int npend = 0;
   const long long n_send = SPLIT ? split_sends(a.g) : 0;
   const long long n_own = SPLIT ? split_owned(a.g) : 0;
-  for (long long s = w; s < a.total_tiles; s += G) {
+  for (long long k = 0, s = pos(0); s < a.total_tiles; s = pos(++k)) {
     if constexpr (!SPLIT) {
       const TileCoord tc = tile_at(a.g, s);
       process<CS, MODE, GS, kPeersDirect>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1,
@@ -872,12 +880,13 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
                                               lds3, tid, wave, lane, nobg, nopv);
       }
     }
-    if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || s + G >= a.total_tiles)) {
+    if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || pos(k + 1) >= a.total_tiles)) {
       wait_vm0();            // this thread's stores have reached the cache
       __syncthreads();
       if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
-        for (long long s2 = fs; s2 <= s; s2 += G) {
+        for (long long k2 = fk; k2 <= k; ++k2) {
+          const long long s2 = pos(k2);
           if constexpr (SPLIT) {
             if (s2 < n_send) signal_chunks(a, send_item(a.g, s2), CS::BM);
           } else {
@@ -886,7 +895,7 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
           }
         }
       }
-      fs = s + G;
+      fk = k + 1;
       npend = 0;
     }
     __syncthreads();   // the staging area is the next item's first stage

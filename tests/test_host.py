@@ -113,6 +113,8 @@ def test_binding_rejects_short_buffers():
         pk._check_sizes(*bufs(S), M, N, K, P, cr, 0)                   # fp32 out in a bf16 buffer
     with pytest.raises(ValueError, match="peer_partials"):
         pk._check_sizes(*bufs(S, peers_rows=S - 1), M, N, K, P, cr, 1)
+    z = torch.empty(0, dtype=bf)
+    pk._check_sizes(z, z, z, z, z, None, 0, 64, 64, 2, 0, 0)   # empty calls touch nothing
 
 
 def test_config_table():
