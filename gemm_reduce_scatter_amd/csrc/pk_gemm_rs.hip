@@ -293,9 +293,9 @@ struct Reader {
   };
 
   __device__ __forceinline__ void read(const unsigned char* st, int kk, Frags& f) const {
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-      f.a[fm] = *reinterpret_cast<const bf16x8*>(st + a_base + fm * 32 * (C::BK * 2) + a_x[kk]);
+    // In the order the MFMAs (fm outer, fn inner) first use them: A0, all of
+    // B, then A1 .. A(FM-1), so the reads issued last are needed last.
+    f.a[0] = *reinterpret_cast<const bf16x8*>(st + a_base + a_x[kk]);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const unsigned char* p = st + b_base[fn] + kk * 16 * (C::BN * 2);
@@ -304,6 +304,9 @@ struct Reader {
       const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
       f.b[fn] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
     }
+#pragma unroll
+    for (int fm = 1; fm < C::FM; ++fm)
+      f.a[fm] = *reinterpret_cast<const bf16x8*>(st + a_base + fm * 32 * (C::BK * 2) + a_x[kk]);
   }
 
   __device__ __forceinline__ static void mfma(const Frags& f, f32x16 (&acc)[C::FM][C::FN]) {
@@ -325,14 +328,16 @@ __device__ __forceinline__ void step_pattern() {
   if constexpr (I < N) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
     if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+    // global loads evenly spaced: after MFMAs 0, N/NV, 2N/NV, ...
+    if constexpr (NV > 0 && (I * NV) % N < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     step_pattern<I + 1, N, NR, NV>();
   }
 }
 
 // One stage of the main loop: MFMA over `cur` in KK k16 steps while a share
-// of the loads of the stage STAGES-1 ahead (into `nxt`) is issued before each
-// step.  Fragments run one step ahead: step kk multiplies the fragments read
+// of the loads of the stage STAGES-1 ahead (into `nxt`) is issued during each
+// step, spaced out among its MFMAs so that the four waves never queue many
+// loads at once.  Fragments run one step ahead: step kk multiplies the fragments read
 // during step kk-1.  The last step first waits for this wave's loads of the
 // next stage, meets the other waves at the barrier (after which every wave
 // has finished reading `cur` and the next stage is complete), reads the
@@ -355,7 +360,10 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
     constexpr int QP = (C::LOADS + C::KK - 1) / C::KK;   // loads issued per k16 step
     constexpr int Q0 = KKI * QP < C::LOADS ? KKI * QP : C::LOADS;
     constexpr int Q1 = (KKI + 1) * QP < C::LOADS ? (KKI + 1) * QP : C::LOADS;
-    ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
+    // With three or more stages the last step's loads wait until after the
+    // barrier, so every step spreads its loads over its MFMAs.
+    constexpr bool LATE = KKI + 1 == C::KK && C::STAGES >= 3;
+    if constexpr (!LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
     bg.template step<STG * C::KK + KKI>(a);
     if constexpr (KKI + 1 < C::KK) {
       rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
@@ -363,16 +371,21 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
       // Every read of `cur` has returned (its fragments feed the MFMAs of
       // this and the previous step), so the barrier also ends all use of it.
       // Loads complete in issue order; younger than the next stage's are
-      // the two stages after it and the background loads of the last two
-      // stages, which may stay in flight.
-      wait_vm<(C::STAGES - 2) * C::LOADS + 2 * C::KK * BG::LOADS_PER_STEP>();
+      // the stages after it issued so far (all but this step's share of the
+      // newest one when it comes late) and the background loads of the last
+      // two stages, which may stay in flight.
+      wait_vm<(C::STAGES - 2) * C::LOADS - (LATE ? Q1 - Q0 : 0) +
+              2 * C::KK * BG::LOADS_PER_STEP>();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      // `nxt` was last read in the stage before this one, before the
+      // previous barrier.
+      if constexpr (LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
       rd.read(nbuf, 0, f[(KKI + 1) & 1]);
     }
     Reader<C>::mfma(f[KKI & 1], acc);
-    step_pattern<0, C::FM * C::FN, C::FM + 2 * C::FN, (KKI + 1 < C::KK) ? Q1 - Q0 : 0>();
+    step_pattern<0, C::FM * C::FN, C::FM + 2 * C::FN, (KKI + 1 < C::KK || LATE) ? Q1 - Q0 : 0>();
     __builtin_amdgcn_sched_barrier(0);
     stage_steps<C, STG, KKI + 1, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc,
                                      f, bg);
