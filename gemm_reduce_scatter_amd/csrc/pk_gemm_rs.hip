@@ -147,17 +147,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, PK_LDS void* dst
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)voff, (int)soff, 0, 0);
 }
 
+// Staged peer partials are read exactly once: non-temporal loads (nt), so
+// they stream past the caches instead of evicting the A and B panels that
+// the main loops of the other workgroups reuse.
+constexpr int kAuxStream = 2;   // cache-policy bits of a buffer load: nt
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 // 16-byte store of output data (send chunks, the owned shard, GEMM-only C),
-// written through the L2 to memory (sc0 sc1): nothing here reads it back,
-// and a device-scope release then has few dirty lines to write back.  The
-// compiler does not see the store, so the wait states a following write of
-// its data registers needs are issued here.
+// written through the L2 to memory (sc0 sc1) as streaming data (nt): nothing
+// here reads it back, and a device-scope release then has few dirty lines to
+// write back.  The compiler does not see the store, so the wait states a
+// following write of its data registers needs are issued here.
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(v)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -582,7 +588,7 @@ struct PresumStream {
 
   __device__ __forceinline__ u32x4 load(uint32_t off_b, int slot) const {
     const uint32_t o = slot < GS ? off_b + (uint32_t)slot * slot_bytes : kOffNone;
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, kAuxStream));
   }
 
   template <int I>
