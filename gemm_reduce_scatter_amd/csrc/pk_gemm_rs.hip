@@ -132,10 +132,12 @@ __device__ __forceinline__ int swz_b(int k) {
   return (((j & 1) << 2) + (j >> 1) * 10) & (CPR - 1);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  // Range 2^31 bytes: offsets of lanes outside the matrix are set to 2^31 and
-  // read as zero.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0x80000000,
+// Buffer descriptor over `bytes` bytes from `base` (at most 2^31).  A load
+// whose vector + scalar offset reaches `bytes` reads zero without touching
+// memory; lanes outside the matrix get a vector offset of 2^31 for that.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes = 0x80000000u) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
 constexpr uint32_t kOffNone = 0x80000000u;
@@ -205,6 +207,10 @@ struct Loader {
   uint32_t b_off;      // byte offset of this lane's B chunk for load 0 at k0 = 0
   int b_k;             // k-row of load 0
   int b_nc;            // n offset (elements) of this lane's B chunk
+  // per item: the vector offsets above, or kOffNone for rows past the shard
+  // (A load q) and columns past N (B)
+  uint32_t a_vo[C::A_LOADS];
+  uint32_t b_vo;
 
   __device__ __forceinline__ void init(const KArgs& a, int wave, int lane) {
     // A: load q of wave w covers LDS rows (q*WAVES + w)*A_RPL .. +A_RPL-1;
@@ -220,6 +226,13 @@ struct Loader {
     b_off = (uint32_t)(b_k * a.N + b_nc) * 2u;
   }
 
+  __device__ __forceinline__ void bind(const KArgs& a, int rows_valid, int col0) {
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q)
+      a_vo[q] = a_row + q * C::WAVES * C::A_RPL < rows_valid ? a_off : kOffNone;
+    b_vo = col0 + b_nc < a.N ? b_off : kOffNone;
+  }
+
   // Per-stage descriptors: A rows from row0, B columns from col0, both at k0.
   struct Stage {
     __amdgpu_buffer_rsrc_t ra, rb;
@@ -229,34 +242,37 @@ struct Loader {
                                          int k0) const {
     Stage st;
     st.ra = make_rsrc(a.A + row0 * a.K + k0);
-    st.rb = make_rsrc(a.B + (long long)k0 * a.N + col0);
+    // B's rows k0 .. K-1 only: the rows past K of a stage (all of them past
+    // the end of K) fall outside the range and read zero.
+    const long long rem = (long long)(a.K - k0) * a.N * 2;
+    st.rb = make_rsrc(a.B + (long long)k0 * a.N + col0,
+                      rem <= 0 ? 0u : rem >= 0x80000000LL ? 0x80000000u : (uint32_t)rem);
     st.k0 = k0;
     return st;
   }
 
   // Issue loads [Q0, Q1) of this wave's A loads followed by its B loads
   // (numbered 0 .. LOADS-1) of one stage into `dst`.  The per-load step is a
-  // scalar offset; lanes outside the matrix (rows past the shard, columns
-  // past N, k past K) get a vector offset past the descriptor range and
-  // load zeros.
+  // scalar offset.  Lanes outside the matrix load zeros: rows past the shard
+  // and columns past N through their vector offsets (bind), B's k-rows past
+  // K through the stage descriptor's range, and A's k-columns past K
+  // (which the range of a row-strided A cannot cut off) through one compare
+  // per call, shared by all A loads of the lane.
   template <int Q0, int Q1>
-  __device__ __forceinline__ void issue(const KArgs& a, const Stage& st, unsigned char* dst,
-                                        int wave, int rows_valid, int col0) const {
+  __device__ __forceinline__ void issue(const KArgs& a, const Stage& st,
+                                        unsigned char* dst, int wave) const {
     const bool a_k_ok = st.k0 + a_kc < a.K;
-    const bool b_n_ok = col0 + b_nc < a.N;
 #pragma unroll
     for (int q = Q0; q < Q1; ++q) {
       if (q < C::A_LOADS) {
-        const bool ok = a_k_ok & (a_row + q * C::WAVES * C::A_RPL < rows_valid);
         const uint32_t soff = (uint32_t)(q * C::WAVES * C::A_RPL) * (uint32_t)a.K * 2u;
-        dma16(st.ra, (PK_LDS void*)(dst + (q * C::WAVES + wave) * 1024), ok ? a_off : kOffNone,
-              soff);
+        dma16(st.ra, (PK_LDS void*)(dst + (q * C::WAVES + wave) * 1024),
+              a_k_ok ? a_vo[q] : kOffNone, soff);
       } else {
         const int qb = q - C::A_LOADS;
-        const bool ok = b_n_ok & (st.k0 + b_k + qb * C::WAVES * C::B_RPL < a.K);
         const uint32_t soff = (uint32_t)(qb * C::WAVES * C::B_RPL) * (uint32_t)a.N * 2u;
-        dma16(st.rb, (PK_LDS void*)(dst + C::A_BYTES + (qb * C::WAVES + wave) * 1024),
-              ok ? b_off : kOffNone, soff);
+        dma16(st.rb, (PK_LDS void*)(dst + C::A_BYTES + (qb * C::WAVES + wave) * 1024), b_vo,
+              soff);
       }
     }
   }
@@ -359,8 +375,7 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
                                             const typename Loader<C>::Stage& ns,
                                             const Reader<C>& rd, const unsigned char* cur,
                                             unsigned char* nxt, const unsigned char* nbuf,
-                                            int wave, int rows_valid, int col0,
-                                            f32x16 (&acc)[C::FM][C::FN],
+                                            int wave, f32x16 (&acc)[C::FM][C::FN],
                                             typename Reader<C>::Frags (&f)[2], BG& bg) {
   if constexpr (KKI < C::KK) {
     constexpr int QP = (C::LOADS + C::KK - 1) / C::KK;   // loads issued per k16 step
@@ -369,7 +384,7 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
     // With three or more stages the last step's loads wait until after the
     // barrier, so every step spreads its loads over its MFMAs.
     constexpr bool LATE = KKI + 1 == C::KK && C::STAGES >= 3;
-    if constexpr (!LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
+    if constexpr (!LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave);
     bg.template step<STG * C::KK + KKI>(a);
     if constexpr (KKI + 1 < C::KK) {
       rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
@@ -387,14 +402,13 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
       asm volatile("" ::: "memory");
       // `nxt` was last read in the stage before this one, before the
       // previous barrier.
-      if constexpr (LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave, rows_valid, col0);
+      if constexpr (LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave);
       rd.read(nbuf, 0, f[(KKI + 1) & 1]);
     }
     Reader<C>::mfma(f[KKI & 1], acc);
     step_pattern<0, C::FM * C::FN, C::FM + 2 * C::FN, (KKI + 1 < C::KK || LATE) ? Q1 - Q0 : 0>();
     __builtin_amdgcn_sched_barrier(0);
-    stage_steps<C, STG, KKI + 1, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc,
-                                     f, bg);
+    stage_steps<C, STG, KKI + 1, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, acc, f, bg);
   }
 }
 
@@ -403,11 +417,10 @@ __device__ __forceinline__ void main_stage(const KArgs& a, const Loader<C>& ld,
                                            const typename Loader<C>::Stage& ns,
                                            const Reader<C>& rd, const unsigned char* cur,
                                            unsigned char* nxt, const unsigned char* nbuf,
-                                           int wave, int rows_valid, int col0,
-                                           f32x16 (&acc)[C::FM][C::FN],
+                                           int wave, f32x16 (&acc)[C::FM][C::FN],
                                            typename Reader<C>::Frags (&f)[2], BG& bg) {
   static_assert(C::KK % 2 == 0, "the next stage's first fragments land in f[0]");
-  stage_steps<C, STG, 0, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, rows_valid, col0, acc, f, bg);
+  stage_steps<C, STG, 0, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, acc, f, bg);
 }
 
 // No background work.
@@ -749,12 +762,12 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
                                         const PV& pv) {
   constexpr int S = C::STAGES;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const long long row0 = (long long)shard * a.S + lrow0;
   Loader<C> ld;
   ld.init(a, wave, lane);
+  ld.bind(a, a.S - lrow0, col0);
   Reader<C> rd;
   rd.init(wm, wn, lane);
-  const long long row0 = (long long)shard * a.S + lrow0;
-  const int rows_valid = a.S - lrow0;
   const int nk = (a.K + C::BK - 1) / C::BK;
 
   f32x16 acc[C::FM][C::FN];
@@ -768,12 +781,9 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   // prologue: stages 0 .. S-2
   constexpr int NQ = C::LOADS;
   if (nk > 0) {
-    ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), b0, wave, rows_valid, col0);
-    if constexpr (S > 2)
-      ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave, rows_valid, col0);
-    if constexpr (S > 3)
-      ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave, rows_valid,
-                               col0);
+    ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), b0, wave);
+    if constexpr (S > 2) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
+    if constexpr (S > 3) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
   }
   using PFT = typename std::conditional<SRC == kPeersPrefetch, PeerPrefetch<C, GS>, NoPeers>::type;
   PFT pf;
@@ -799,7 +809,7 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
 #define PK_STEP(I)                                                                           \
   main_stage<C, (I), BG>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,     \
                          pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3), \
-                         pick<((I) + 1) % S>(b0, b1, b2, b3), wave, rows_valid, col0, acc, f, bg)
+                         pick<((I) + 1) % S>(b0, b1, b2, b3), wave, acc, f, bg)
       PK_STEP(0);
       PK_STEP(1);
       if constexpr (S > 2) PK_STEP(2);
