@@ -1,8 +1,10 @@
 """Benchmark of one GPU's share of the fused bf16 GEMM + reduce-scatter.
 
-One step = re-zero the chunk flags + one fused call (local GEMM, bf16 send
-chunks with ready flags, owned-shard sum of the staged peer partials) over
-one batch of synthetic inputs resident in HBM.  Prints ONE JSON line.
+One step = one fused call (local GEMM, bf16 send chunks with ready flags,
+owned-shard sum of the staged peer partials) over one batch of synthetic
+inputs resident in HBM.  Ready words count calls, so nothing is cleared
+between steps; after the run every ready word of a buffer set equals the
+number of calls made on it.  Prints ONE JSON line.
 
 Default workload: P = 8, rank 3, M = N = 4096, K = 512 (the HBM-bound,
 communication-dominant case), rotating buffer sets so the 256 MB
@@ -79,25 +81,26 @@ class BufferSet:
 
 
 def time_steps(fn, n_sets, warmup, steps, torch):
-    """Run warmup + timed steps; returns (ms per step, mean kernel ms)."""
+    """Run warmup + timed steps; returns (ms per step, wall seconds).
+
+    A step is one launch of the kernel, issued through a pre-bound call so the
+    host stays ahead of the GPU; HIP events on the launch stream bracket the
+    whole timed region, so ms per step is the kernel's average duration in a
+    back-to-back stream of launches (inter-launch gaps included).
+    """
     for i in range(warmup):
-        fn(i % n_sets, None)
+        fn(i % n_sets)
     torch.cuda.synchronize()
-    ks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ke = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        fn((warmup + i) % n_sets, (ks[i], ke[i]))
+        fn((warmup + i) % n_sets)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = t_start.elapsed_time(t_end) / steps
-    k_ms = sum(a.elapsed_time(b) for a, b in zip(ks, ke)) / steps
-    return ms_step, k_ms, wall
+    return t_start.elapsed_time(t_end) / steps, wall
 
 
 def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_only=True,
@@ -115,34 +118,30 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
     opts = dict(config=args.config, max_workgroups=args.max_workgroups, group_n=args.group_n)
     fused_opts = dict(opts, owned_split=args.owned_split)
 
-    def step(i, ev):
-        s = sets[i]
-        s.flags.zero_()
-        if ev:
-            ev[0].record()
-        pk.pk_gemm_rs_local_ex(s.A, s.B, s.peers, s.send, s.out, s.flags, w.M, w.N, w.K, w.P,
-                               w.rank, chunk, order, out_bf16, **fused_opts)
-        if ev:
-            ev[1].record()
+    calls = [0] * n_sets
+    launch = [pk.BoundCall(s.A, s.B, s.peers, s.send, s.out, s.flags, w.M, w.N, w.K, w.P,
+                           w.rank, chunk, order, out_bf16, **fused_opts) for s in sets]
 
-    ms_step, k_ms, wall = time_steps(step, n_sets, warmup, steps, torch)
-    # every flag must be raised after the last call
-    assert all(int(s.flags[: s.flags.numel() // 2].min()) == 1 for s in sets)
+    def step(i):
+        launch[i]()
+        calls[i] += 1
+
+    ms_step, wall = time_steps(step, n_sets, warmup, steps, torch)
+    k_ms = ms_step
+    # every ready word counts the calls on its set; every counter is back to 0
+    for s, n in zip(sets, calls):
+        half = s.flags.numel() // 2
+        assert int(s.flags[:half].min()) == n and int(s.flags[:half].max()) == n
+        assert int(s.flags[half:].abs().max()) == 0
     res = dict(ms_per_step=ms_step, kernel_ms=k_ms, wall_s=wall, n_sets=n_sets,
                chunk_rows=chunk, tile_order=order)
     if gemm_only:
         for s in sets:
             s.gemm_out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
 
-        def gstep(i, ev):
-            s = sets[i]
-            if ev:
-                ev[0].record()
-            pk.pk_gemm_rs_local_ex(s.A, s.B, None, None, s.gemm_out, None, w.M, w.N, w.K, w.P,
-                                   0, 0, 0, 1, gemm_only=True, **opts)
-            if ev:
-                ev[1].record()
-        _, g_ms, _ = time_steps(gstep, n_sets, warmup, steps, torch)
+        glaunch = [pk.BoundCall(s.A, s.B, None, None, s.gemm_out, None, w.M, w.N, w.K, w.P,
+                                0, 0, 0, 1, gemm_only=True, **opts) for s in sets]
+        g_ms, _ = time_steps(lambda i: glaunch[i](), n_sets, warmup, steps, torch)
         res["gemm_only_kernel_ms"] = g_ms
         res["exposed_fraction"] = metrics.exposed_fraction(k_ms, g_ms)
     del sets

@@ -190,6 +190,32 @@ def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, 
         int(out_bf16), ctypes.byref(o), _stream(stream)))
 
 
+class BoundCall:
+    """pk_gemm_rs_local_ex with its tensors checked and its arguments marshalled
+    once.  Calling the object launches the share again on ``stream`` (fixed at
+    construction; None = torch's current stream at that time) with the same
+    buffers, so a loop of launches pays only the foreign call.  The tensors
+    must stay alive and unmoved while the object is used."""
+
+    def __init__(self, A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
+                 chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0, group_n=0,
+                 gemm_only=False, owned_split=0, signal_batch=0, stream=None):
+        _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+        _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
+                     out_bf16, gemm_only)
+        self._keep = (A, B, peer_partials, send_bufs, out, flags)
+        self._opts = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
+        self._fn = load().pk_gemm_rs_local_ex
+        self._args = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out),
+                      _ptr(flags), int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),
+                      int(tile_order), int(out_bf16), ctypes.byref(self._opts), _stream(stream))
+        code = load().pk_validate(*self._args[:14], ctypes.byref(self._opts))
+        _check(code)
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._args))
+
+
 def pk_flags_words(P, M, chunk_rows) -> int:
     return _check(load().pk_flags_words(int(P), int(M), int(chunk_rows)))
 

@@ -449,8 +449,10 @@ __device__ __forceinline__ unsigned char* pick(unsigned char* b0, unsigned char*
 // every chunk the tile touches.  Each arrival is relaxed: the data it vouches
 // for was released before it.  The arrival that completes a chunk acquires
 // (so the other workgroups' released stores happen before what follows),
-// publishes the ready word with a release store and resets the counter for
-// the next launch.
+// adds one to the ready word with release (the pages' signal adds to a
+// counter and their wait waits for it to reach a value: call n of a flags
+// buffer raises its ready words to n, and nothing has to clear them between
+// calls) and resets the counter for the next launch.
 __device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& tc, int BM) {
   int c0, c1;
   chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
@@ -464,7 +466,7 @@ __device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& t
                                                 __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1u == want) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&counters[idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

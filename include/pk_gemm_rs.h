@@ -12,10 +12,12 @@
  *
  *   C_loc = A * B                      bf16 inputs, fp32 accumulation (MFMA)
  *   for every other rank d: send slot j(d) <- bf16(C_loc rows of shard d)
- *       and, per chunk of `chunk_rows` rows, a ready word set to 1 once every
- *       tile of the chunk is stored (the pages' signal primitive; chunks as
- *       in "Syncopate: Efficient Multi-GPU AI Kernels via Automatic Chunk-
- *       Centric Compute-Communication Overlap", section 5.1);
+ *       and, per chunk of `chunk_rows` rows, a ready word raised by one once
+ *       every tile of the chunk is stored (the pages' signal primitive,
+ *       "The Eight PK Primitives": signal adds to a counter, wait waits for
+ *       it to reach a value; chunks as in "Syncopate: Efficient Multi-GPU AI
+ *       Kernels via Automatic Chunk-Centric Compute-Communication Overlap",
+ *       section 5.1);
  *   out <- sum_j peer_partials[j] + C_loc rows of shard `rank`   (fp32: the
  *       peers added in ascending slot order starting from +0, then the
  *       local partial), stored once.
@@ -30,9 +32,12 @@
  *    j if j < rank, else rank j+1 (ascending ranks, skipping `rank`).
  *  - flags: uint32 [pk_flags_words(P, M, chunk_rows)]: first (P-1)*C ready
  *    words (slot-major, C = S / chunk_rows chunks per slot), then (P-1)*C
- *    arrival counters.  All words must be zero at launch.  When the stream
- *    reaches the end of the call every ready word is 1 and every counter is 0
- *    again, whatever the tile configuration or tile order.
+ *    arrival counters.  Counters must be zero at launch, and are zero again
+ *    when the stream reaches the end of the call.  Each call adds exactly 1
+ *    to every ready word (wrapping at 2^32), whatever the tile
+ *    configuration or tile order: zero the buffer once, and the n-th call on
+ *    it leaves every ready word at n, so a consumer of that call waits for
+ *    n.  Nothing needs to be cleared between calls.
  *  - Pointers are device pointers owned by the caller, 16-byte aligned; the
  *    output buffers (send_bufs, out, flags) must not overlap each other or
  *    the inputs.  Unused pointers may be NULL: peer_partials, send_bufs and

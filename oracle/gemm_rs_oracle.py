@@ -31,7 +31,8 @@ Definition implemented (one rank ``rank`` of ``P``; S = M / P):
     send[j]    = bf16_rne(C[d*S:(d+1)*S, :])  for every destination d != rank,
                                               slot j = d if d < rank else d - 1
     out        = C[rank*S:(rank+1)*S, :] + sum_j peers[j]   (j ascending)
-    ready[j,c] = 1, counter[j,c] = 0          for every slot j and chunk c
+    ready[j,c] = ready_before[j,c] + 1,       for every slot j and chunk c
+    counter[j,c] = 0
 
 The pages fix the mathematics (the owner ends with the sum over all ranks of
 their partials for its shard) but not the buffer layout, the rounding mode of
@@ -44,8 +45,12 @@ the bf16 send copy, or the flag words; the readings taken here are:
 * chunk c of a slot is rows [c*chunk_rows, (c+1)*chunk_rows) of that slot, at
   full width N;
 * the owned shard sums the staged peer partials in ascending slot order;
-* after the call every chunk's ready word is exactly 1 and its arrival
-  counter is back to 0.
+* a chunk's ready word counts the times it was published: the pages' signal
+  primitive ("The Eight PK Primitives" in the ParallelKittens summary page)
+  atomically adds a value to a barrier counter and wait spins until the
+  counter reaches an expected value, so each call adds exactly 1 to every
+  chunk's ready word (from zero for fresh flags) and leaves its arrival
+  counter back at 0.
 
 Everything is computed in fp64.  The matrix product is a library primitive
 (numpy ``matmul`` in float64); every other step is written out here.
@@ -202,7 +207,7 @@ class OracleResult:
 
 
 def reduce_scatter_share(C: np.ndarray, peers: np.ndarray, P: int, rank: int,
-                         chunk_rows: int) -> OracleResult:
+                         chunk_rows: int, ready_before=None) -> OracleResult:
     """Reduce-scatter share of rank ``rank`` given its local partial C.
 
     [PK] "Scheduling Analysis": each output row block goes to the rank that
@@ -210,7 +215,8 @@ def reduce_scatter_share(C: np.ndarray, peers: np.ndarray, P: int, rank: int,
     (float64 [P-1, S, N]) are the partials that the other ranks sent to this
     rank, slot j coming from rank dest_of_slot(j).  [SYN] 5.1: each slot is
     split into chunks of ``chunk_rows`` full-width rows, each a unit whose
-    readiness is signalled once.
+    readiness is signalled once per call: its ready word goes up by one from
+    ``ready_before`` (uint32 [P-1, S/chunk_rows], zeros when None).
     """
     M, N = C.shape
     if P < 1 or not (0 <= rank < P):
@@ -235,17 +241,22 @@ def reduce_scatter_share(C: np.ndarray, peers: np.ndarray, P: int, rank: int,
         out = out + peers[j]
 
     n_chunks = S // chunk_rows
-    ready = np.ones((P - 1, n_chunks), dtype=np.uint32)
+    if ready_before is None:
+        ready_before = np.zeros((P - 1, n_chunks), dtype=np.uint32)
+    ready_before = np.asarray(ready_before, dtype=np.uint32)
+    if ready_before.shape != (P - 1, n_chunks):
+        raise ValueError(f"ready_before must have shape {(P - 1, n_chunks)}")
+    ready = ready_before + np.uint32(1)    # uint32 arithmetic wraps like the device word
     counters = np.zeros((P - 1, n_chunks), dtype=np.uint32)
     return OracleResult(send_bits=send, out=out, ready=ready, counters=counters, C=C)
 
 
 def gemm_rs_oracle(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits: np.ndarray,
-                   P: int, rank: int, chunk_rows: int) -> OracleResult:
+                   P: int, rank: int, chunk_rows: int, ready_before=None) -> OracleResult:
     """Whole share from bf16 inputs: local partial, send copies, owned sum, flags."""
     C = local_partial(A_bits, B_bits)
     peers = bf16_bits_to_f64(peer_bits)
-    return reduce_scatter_share(C, peers, P, rank, chunk_rows)
+    return reduce_scatter_share(C, peers, P, rank, chunk_rows, ready_before)
 
 
 def gemm_rs_elements(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits, P: int,

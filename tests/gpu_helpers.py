@@ -86,12 +86,13 @@ def host(share: Share):
     return send, out, out_bits, flags
 
 
-def expected_flags(w: gen.Workload, chunk_rows: int) -> np.ndarray:
-    """Closed form after a call: every ready word 1, every counter 0."""
+def expected_flags(w: gen.Workload, chunk_rows: int, calls: int = 1) -> np.ndarray:
+    """Closed form after `calls` calls on zeroed flags: every ready word equals
+    `calls` (one signal per chunk per call), every counter 0."""
     if w.S == 0 or w.P == 1:
         return np.zeros(0, np.uint32)
     n = (w.P - 1) * (w.S // chunk_rows)
-    return np.concatenate([np.ones(n, np.uint32), np.zeros(n, np.uint32)])
+    return np.concatenate([np.full(n, calls, np.uint32), np.zeros(n, np.uint32)])
 
 
 def compare_real(res: orc.OracleResult, mag_C, share: Share, n_terms: int):
@@ -99,7 +100,8 @@ def compare_real(res: orc.OracleResult, mag_C, share: Share, n_terms: int):
     send, out, _, flags = host(share)
     w = share.w
     S = w.S
-    assert np.array_equal(flags, expected_flags(w, share.chunk_rows)), "flags"
+    want = res.flags if (w.S > 0 and w.P > 1) else np.zeros(0, np.uint32)
+    assert np.array_equal(flags, want), "flags"
     bf16_out = share.out_dtype == "bf16"
     # owned shard
     own_mag = mag_C[w.rank * S:(w.rank + 1) * S]
@@ -134,7 +136,8 @@ def compare_exact(res: orc.OracleResult, share: Share):
     """Integer-valued inputs: every output bit must match the oracle."""
     send, out, out_bits, flags = host(share)
     w = share.w
-    assert np.array_equal(flags, expected_flags(w, share.chunk_rows)), "flags"
+    want = res.flags if (w.S > 0 and w.P > 1) else np.zeros(0, np.uint32)
+    assert np.array_equal(flags, want), "flags"
     if w.P > 1:
         assert np.array_equal(send, res.send_bits), "send buffers differ"
     if share.out_dtype == "f32":

@@ -224,13 +224,38 @@ def test_outputs_invariant_across_orders_chunks_and_runs():
                 else:
                     assert torch.equal(cur[0], ref[0]), (chunk, order, grid, split)
                     assert torch.equal(cur[1].view(torch.int32), ref[1].view(torch.int32))
-    # a repeat call on the same buffers after re-zeroing the flags
+    # repeat calls on the same buffers, flags never cleared: each call raises
+    # every ready word by one and leaves the counters at zero
     share = H.Share(CD, "f32")
-    for _ in range(3):
-        share.reset_flags()
-        H.run(share, A, B, peers)
-    torch.cuda.synchronize()
+    for n in range(1, 4):
+        H.run(share, A, B, peers, owned_split=(0, -1, 1)[n - 1])
+        torch.cuda.synchronize()
+        assert torch.equal(share.flags.cpu(), torch.from_numpy(
+            H.expected_flags(CD, CD.chunk_rows, calls=n).view(np.int32)))
     assert torch.equal(share.send.view(torch.int16), ref[0])
+    assert torch.equal(share.out.view(torch.int32), ref[1].view(torch.int32))
+
+
+def test_bound_call_relaunches_the_same_share():
+    w = gen.Workload("bound", P=4, rank=2, M=1024, N=768, K=320, chunk_rows=64,
+                     ab_dist="int", peer_dist="int", out_dtype="f32")
+    A, B, peers = gen.make_inputs(w, DEV, seed=21, integer=True)
+    share = H.Share(w, "f32")
+    call = pk.BoundCall(A, B, peers, share.send, share.out, share.flags, w.M, w.N, w.K, w.P,
+                        w.rank, w.chunk_rows, 2, 0, owned_split=1)
+    ready = None
+    for n in (1, 2):
+        call()
+        torch.cuda.synchronize()
+        res = orc.gemm_rs_oracle(gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers), w.P,
+                                 w.rank, w.chunk_rows, ready_before=ready)
+        H.compare_exact(res, share)   # integer inputs: every output and flag exact
+        assert np.array_equal(share.flags.cpu().numpy().view(np.uint32),
+                              H.expected_flags(w, w.chunk_rows, calls=n))
+        ready = res.ready
+    with pytest.raises(ValueError):
+        pk.BoundCall(A, B, peers, share.send, share.out[:10], share.flags, w.M, w.N, w.K, w.P,
+                     w.rank, w.chunk_rows, 2, 0)
 
 
 def test_virtual_ranks_reduce_scatter_on_one_gpu():

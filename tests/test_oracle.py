@@ -278,6 +278,21 @@ def test_flags_closed_form():
     assert np.array_equal(res.flags, np.array([1] * 12 + [0] * 12, np.uint32))
 
 
+def test_ready_words_count_calls():
+    """Signal adds one per call (ParallelKittens summary page, "The Eight PK
+    Primitives": signal adds to a counter, wait waits for it to reach a value)."""
+    rng = np.random.default_rng(5)
+    A, B = _int_mats(rng, 64, 4, 8)
+    peers = np.zeros((3, 16, 8), np.uint16)
+    before = np.array([[0, 1, 2, 7], [5, 5, 5, 5], [0xFFFFFFFF, 0, 3, 9]], np.uint32)
+    res = orc.gemm_rs_oracle(_bits(A), _bits(B), peers, 4, 3, 4, ready_before=before)
+    assert np.array_equal(res.ready, np.array([[1, 2, 3, 8], [6, 6, 6, 6], [0, 1, 4, 10]],
+                                              np.uint32))
+    assert np.all(res.counters == 0)
+    with pytest.raises(ValueError):
+        orc.gemm_rs_oracle(_bits(A), _bits(B), peers, 4, 3, 4, ready_before=before[:2])
+
+
 def test_bad_arguments_rejected():
     C = np.zeros((8, 2))
     with pytest.raises(ValueError):
