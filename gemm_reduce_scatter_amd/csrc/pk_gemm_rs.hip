@@ -446,29 +446,51 @@ __device__ __forceinline__ unsigned char* pick(unsigned char* b0, unsigned char*
 // Ready-word protocol (the pages' signal primitive, per chunk).  A caller
 // has made the stores of one or more finished send tiles visible at device
 // scope with a release fence; for each tile it then adds one arrival to
-// every chunk the tile touches.  Each arrival is relaxed: the data it vouches
+// every chunk the tile touches (signal_chunk, one per pair).  Each arrival is relaxed: the data it vouches
 // for was released before it.  The arrival that completes a chunk acquires
 // (so the other workgroups' released stores happen before what follows),
 // adds one to the ready word with release (the pages' signal adds to a
 // counter and their wait waits for it to reach a value: call n of a flags
 // buffer raises its ready words to n, and nothing has to clear them between
 // calls) and resets the counter for the next launch.
-__device__ __forceinline__ void signal_chunks(const KArgs& a, const TileCoord& tc, int BM) {
-  int c0, c1;
-  chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
-  const int slot = slot_of(tc.shard, a.rank);
+__device__ __forceinline__ void signal_chunk(const KArgs& a, int idx, uint32_t want) {
   uint32_t* ready = a.flags;
   uint32_t* counters = a.flags + (long long)(a.P - 1) * a.n_chunks;
-  for (int c = c0; c <= c1; ++c) {
-    const int idx = slot * a.n_chunks + c;
-    const uint32_t want = expected_arrivals(c, BM, a.chunk_rows, a.g.Tn);
-    const uint32_t old = __hip_atomic_fetch_add(&counters[idx], 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1u == want) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_fetch_add(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&counters[idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t old = __hip_atomic_fetch_add(&counters[idx], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1u == want) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __hip_atomic_fetch_add(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&counters[idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Arrivals of a batch of finished send tiles, spread over the lanes of one
+// wave: the batch's (tile, chunk) pairs are numbered in walk order and lane
+// l takes pairs l, l+64, ..., so the arrivals of up to 64 pairs travel in
+// one vector atomic instead of one after another.  `tile_of(k2, tc)` gives
+// the send tile of round k2 (false for an owned item).
+template <class TileOf>
+__device__ __forceinline__ void signal_batch(const KArgs& a, long long fk, long long k, int BM,
+                                             int lane, const TileOf& tile_of) {
+  for (int base = 0;; base += 64) {
+    int n = 0, idx = -1;
+    uint32_t want = 0;
+    for (long long k2 = fk; k2 <= k; ++k2) {
+      TileCoord tc;
+      if (!tile_of(k2, tc)) continue;
+      int c0, c1;
+      chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
+      const int slot = slot_of(tc.shard, a.rank);
+      for (int c = c0; c <= c1; ++c, ++n) {
+        if (n == base + lane) {
+          idx = slot * a.n_chunks + c;
+          want = expected_arrivals(c, BM, a.chunk_rows, a.g.Tn);
+        }
+      }
     }
+    if (idx >= 0) signal_chunk(a, idx, want);
+    if (n <= base + 64) break;
   }
 }
 
@@ -914,17 +936,19 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
     if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || pos(k + 1) >= a.total_tiles)) {
       wait_vm0();            // this thread's stores have reached the cache
       __syncthreads();
-      if (tid == 0) {
+      if (wave == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
-        for (long long k2 = fk; k2 <= k; ++k2) {
+        signal_batch(a, fk, k, CS::BM, lane, [&](long long k2, TileCoord& tc) {
           const long long s2 = pos(k2);
           if constexpr (SPLIT) {
-            if (s2 < n_send) signal_chunks(a, send_item(a.g, s2), CS::BM);
+            if (s2 >= n_send) return false;
+            tc = send_item(a.g, s2);
+            return true;
           } else {
-            const TileCoord t2 = tile_at(a.g, s2);
-            if (t2.shard != a.rank) signal_chunks(a, t2, CS::BM);
+            tc = tile_at(a.g, s2);
+            return tc.shard != a.rank;
           }
-        }
+        });
       }
       fk = k + 1;
       npend = 0;
