@@ -899,16 +899,42 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   int npend = 0;
   const long long n_send = SPLIT ? split_sends(a.g) : 0;
   const long long n_own = SPLIT ? split_owned(a.g) : 0;
+  // Release the pending send tiles of rounds fk .. k and raise their chunks.
+  const auto flush = [&](long long k) {
+    wait_vm0();            // this thread's stores have reached the cache
+    __syncthreads();
+    if (wave == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
+      signal_batch(a, fk, k, CS::BM, lane, [&](long long k2, TileCoord& tc) {
+        const long long s2 = pos(k2);
+        if constexpr (SPLIT) {
+          if (s2 >= n_send) return false;
+          tc = send_item(a.g, s2);
+          return true;
+        } else {
+          tc = tile_at(a.g, s2);
+          return tc.shard != a.rank;
+        }
+      });
+    }
+    fk = k + 1;
+    npend = 0;
+  };
   for (long long k = 0, s = pos(0); s < a.total_tiles; s = pos(++k)) {
+    const bool last = pos(k + 1) >= a.total_tiles;
     if constexpr (!SPLIT) {
       const TileCoord tc = tile_at(a.g, s);
       process<CS, MODE, GS, kPeersDirect>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1,
                                           lds2, lds3, tid, wave, lane, nobg, nopv);
       if (MODE == kFused && tc.shard != a.rank) ++npend;
+      if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || last)) flush(k);
     } else {
       const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
       if (s < n_send) {
         const TileCoord st = send_item(a.g, s);
+        // A send tile's batch is released before the owned sub-tile that
+        // rides with it, so the wait covers only send stores and the ready
+        // words rise a sub-tile earlier.
         if (s < n_own) {
           const TileCoord ot = owned_item(a.g, s);
           const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
@@ -917,41 +943,23 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
           ps.init(a, olr, oc, wm, wn, lane);
           process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, ps, nopv);
+          if (++npend >= a.sig_batch || last) flush(k);
           __syncthreads();   // the staging area is the sub-tile's first stage
           process<CO, MODE, GS, kPeersPresum>(a, ot.shard, olr, oc, lds0, lds1, lds2, lds3, tid,
                                               wave, lane, nobg, ps);
         } else {
           process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
+          if (++npend >= a.sig_batch || last) flush(k);
         }
-        ++npend;
       } else {
         const TileCoord ot = owned_item(a.g, s);
         const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
         process<CO, MODE, GS, kPeersPrefetch>(a, ot.shard, ot.t * CS::BM + sm * CO::BM,
                                               ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
                                               lds3, tid, wave, lane, nobg, nopv);
+        if (npend > 0 && last) flush(k);
       }
-    }
-    if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || pos(k + 1) >= a.total_tiles)) {
-      wait_vm0();            // this thread's stores have reached the cache
-      __syncthreads();
-      if (wave == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
-        signal_batch(a, fk, k, CS::BM, lane, [&](long long k2, TileCoord& tc) {
-          const long long s2 = pos(k2);
-          if constexpr (SPLIT) {
-            if (s2 >= n_send) return false;
-            tc = send_item(a.g, s2);
-            return true;
-          } else {
-            tc = tile_at(a.g, s2);
-            return tc.shard != a.rank;
-          }
-        });
-      }
-      fk = k + 1;
-      npend = 0;
     }
     __syncthreads();   // the staging area is the next item's first stage
   }
