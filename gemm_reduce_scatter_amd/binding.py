@@ -29,7 +29,8 @@ class PkError(RuntimeError):
 class _Options(ctypes.Structure):
     _fields_ = [("config", ctypes.c_int), ("max_workgroups", ctypes.c_int),
                 ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int),
-                ("owned_split", ctypes.c_int), ("signal_batch", ctypes.c_int)]
+                ("owned_split", ctypes.c_int), ("signal_batch", ctypes.c_int),
+                ("ready_clock", ctypes.c_void_p)]
 
 
 def lib_path() -> str:
@@ -74,6 +75,9 @@ def load():
     lib.pk_strerror.restype = ctypes.c_char_p
     lib.pk_version.argtypes = []
     lib.pk_version.restype = i32
+    lib.pk_rs_consume.argtypes = [vp, vp, vp, i64, i64, i32, i32, ctypes.c_uint32, i32, vp, vp,
+                                  i32, vp]
+    lib.pk_rs_consume.restype = i32
     del u32p
     _lib = lib
     return lib
@@ -105,9 +109,10 @@ def _stream(stream):
 
 
 def _opts(config=0, max_workgroups=0, group_n=0, gemm_only=False, owned_split=0,
-          signal_batch=0):
+          signal_batch=0, ready_clock=None):
     return _Options(int(config), int(max_workgroups), int(group_n), 1 if gemm_only else 0,
-                    int(owned_split), int(signal_batch))
+                    int(owned_split), int(signal_batch),
+                    None if ready_clock is None else ready_clock.data_ptr())
 
 
 def _check_tensors(A, B, peer_partials, send_bufs, out, flags):
@@ -178,16 +183,72 @@ def pk_gemm_rs_local_bf16out(A, B, peer_partials, send_bufs, out, flags, M, N, K
 def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                         chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0,
                         group_n=0, gemm_only=False, owned_split=0, signal_batch=0,
-                        stream=None) -> int:
-    """Fused share with explicit tile configuration / grid / grouping options."""
+                        ready_clock=None, stream=None) -> int:
+    """Fused share with explicit tile configuration / grid / grouping options.
+
+    ready_clock: None or a device int64 tensor of (P-1)*S/chunk_rows words that
+    receives the device clock at which each chunk's ready word rose."""
     _check_tensors(A, B, peer_partials, send_bufs, out, flags)
     _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows, out_bf16,
                  gemm_only)
-    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
+    _check_clock(ready_clock, M, P, chunk_rows, gemm_only)
+    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch, ready_clock)
     return _check(load().pk_gemm_rs_local_ex(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
         int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
         int(out_bf16), ctypes.byref(o), _stream(stream)))
+
+
+def _chunks(M, P, chunk_rows) -> int:
+    M, P, chunk_rows = int(M), int(P), int(chunk_rows)
+    if P < 2 or M <= 0 or chunk_rows <= 0 or M % P or (M // P) % chunk_rows:
+        return 0
+    return (P - 1) * ((M // P) // chunk_rows)
+
+
+def _check_clock(ready_clock, M, P, chunk_rows, gemm_only=False):
+    import torch
+    if ready_clock is None:
+        return
+    if gemm_only:
+        raise ValueError("ready_clock needs the fused share (gemm_only off)")
+    if not ready_clock.is_cuda or not ready_clock.is_contiguous() or \
+            ready_clock.dtype not in (torch.int64, torch.uint64):
+        raise ValueError("ready_clock must be a contiguous 64-bit device tensor")
+    if ready_clock.numel() < _chunks(M, P, chunk_rows):
+        raise ValueError("ready_clock needs one word per chunk")
+
+
+def pk_rs_consume(flags, send_bufs, dest, M, N, P, chunk_rows, expected, status,
+                  observed=None, spin_limit=1 << 16, max_workgroups=0, stream=None) -> int:
+    """Chunk consumer: wait for each chunk's ready word to reach `expected`,
+    then copy the chunk from send_bufs to dest (see pk_gemm_rs.h)."""
+    import torch
+    for name, t in (("flags", flags), ("send_bufs", send_bufs), ("dest", dest),
+                    ("status", status), ("observed", observed)):
+        if t is None:
+            if name != "observed":
+                raise ValueError(f"{name} is required")
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    n = _chunks(M, P, chunk_rows)
+    if n > 0:
+        S = int(M) // int(P)
+        need = 2 * (int(P) - 1) * S * int(N)
+        for name, t in (("send_bufs", send_bufs), ("dest", dest)):
+            if t.numel() * t.element_size() < need:
+                raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {need}")
+        if flags.numel() * flags.element_size() < 4 * n:
+            raise ValueError("flags is shorter than the ready words")
+        if status.dtype != torch.int32 or status.numel() < n:
+            raise ValueError("status must be int32 with one word per chunk")
+        if observed is not None and (observed.element_size() != 8 or observed.numel() < n):
+            raise ValueError("observed must be 64-bit with one word per chunk")
+    return _check(load().pk_rs_consume(
+        _ptr(flags), _ptr(send_bufs), _ptr(dest), int(M), int(N), int(P), int(chunk_rows),
+        ctypes.c_uint32(int(expected) & 0xFFFFFFFF), int(spin_limit), _ptr(status),
+        _ptr(observed), int(max_workgroups), _stream(stream)))
 
 
 class BoundCall:
@@ -199,12 +260,15 @@ class BoundCall:
 
     def __init__(self, A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                  chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0, group_n=0,
-                 gemm_only=False, owned_split=0, signal_batch=0, stream=None):
+                 gemm_only=False, owned_split=0, signal_batch=0, ready_clock=None,
+                 stream=None):
         _check_tensors(A, B, peer_partials, send_bufs, out, flags)
         _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
                      out_bf16, gemm_only)
-        self._keep = (A, B, peer_partials, send_bufs, out, flags)
-        self._opts = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
+        _check_clock(ready_clock, M, P, chunk_rows, gemm_only)
+        self._keep = (A, B, peer_partials, send_bufs, out, flags, ready_clock)
+        self._opts = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch,
+                           ready_clock)
         self._fn = load().pk_gemm_rs_local_ex
         self._args = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out),
                       _ptr(flags), int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),

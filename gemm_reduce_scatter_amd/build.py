@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "pk_gemm_rs.hip")
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("pk_gemm_rs.hip", "pk_consume.hip")]
 OUT = os.path.join(HERE, "libpk_gemm_rs.so")
 
 HIPCC_FLAGS = [
@@ -31,7 +31,7 @@ def hipcc() -> str:
 
 def build_library(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

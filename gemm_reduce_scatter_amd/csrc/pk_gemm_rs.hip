@@ -111,6 +111,7 @@ struct KArgs {
   int P, rank, S, chunk_rows, n_chunks;
   int out_bf16;
   int sig_batch;       // send tiles per ready-word release (>= 1)
+  uint64_t* ready_clock;   // null, or [P-1][n_chunks]: device clock when a ready word rose
   Grid g;
   long long total_tiles;
 };
@@ -462,6 +463,7 @@ __device__ __forceinline__ void signal_chunk(const KArgs& a, int idx, uint32_t w
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __hip_atomic_fetch_add(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&counters[idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.ready_clock) a.ready_clock[idx] = wall_clock64();
   }
 }
 
@@ -1032,6 +1034,8 @@ static int validate(const void* A, const void* B, const void* peers, const void*
   if (o && (o->max_workgroups < 0 || o->group_n < 0)) return PK_ERR_CONFIG;
   if (o && (o->owned_split < -1 || o->owned_split > 1)) return PK_ERR_CONFIG;
   if (o && o->signal_batch < 0) return PK_ERR_CONFIG;
+  if (o && o->ready_clock && (reinterpret_cast<uintptr_t>(o->ready_clock) & 7u))
+    return PK_ERR_POINTER;
   if (M == 0 || N == 0) return PK_OK;     // nothing to write
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };
   if (!need(out)) return PK_ERR_POINTER;
@@ -1173,6 +1177,7 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.g.N = (int)N;
   a.g.order = tile_order;
   a.sig_batch = (o && o->signal_batch > 0) ? o->signal_batch : kDefaultSignalBatch;
+  a.ready_clock = o ? o->ready_clock : nullptr;
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg) {

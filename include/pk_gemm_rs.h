@@ -107,6 +107,9 @@ typedef struct pk_options {
                            share one device-scope release, 0 = auto (8).  Larger
                            batches cost fewer cache writebacks and raise ready words
                            later; the last batch of a workgroup is always flushed. */
+  uint64_t* ready_clock; /* NULL, or uint64 [P-1][S/chunk_rows] (8-byte aligned): for
+                           each chunk, the 100 MHz device clock when its ready word
+                           rose in this call (timing of the chunk consumer only). */
 } pk_options;
 
 /* The fused share with explicit options; out_bf16 selects bf16 (1) or fp32 (0)
@@ -116,6 +119,37 @@ int pk_gemm_rs_local_ex(const void* A, const void* B, const void* peer_partials,
                         int64_t M, int64_t N, int64_t K, int P, int rank,
                         int chunk_rows, int tile_order, int out_bf16,
                         const pk_options* opts, void* stream);
+
+/* Chunk consumer: the transfer half of the reduce-scatter, the step after
+ * the fused share ("The Eight PK Primitives" of the ParallelKittens summary
+ * page: wait spins on a counter until it reaches an expected value; chunks
+ * as in Syncopate section 5.1, moved as one unit once their tiles are
+ * stored).  For every send slot j and chunk c (slot-major order, the order
+ * the row-major walk completes them) it waits until the chunk's ready word
+ * reaches `expected` (compared as a signed 32-bit distance, so counts may
+ * wrap), acquires at device scope, and copies rows [c*chunk_rows,
+ * (c+1)*chunk_rows) of send_bufs[j] into dest[j]: the staging buffer of the
+ * rank that owns those rows in a multi-GPU run.
+ *  - flags: the producer's flags buffer (ready words read, nothing written).
+ *  - send_bufs, dest: bf16 [P-1][S][N], 16-byte aligned, not overlapping.
+ *  - expected: the ready value of the producer call to consume (n for the
+ *    n-th call on a zeroed flags buffer).
+ *  - spin_limit >= 1: polls of one ready word (about 1-2 us apart) before
+ *    the chunk is given up: then its status is 1 and its dest rows are not
+ *    touched, so a producer that never signals cannot hang the consumer.
+ *  - status: int32 [P-1][S/chunk_rows], per chunk 0 (copied) or 1 (timed out).
+ *  - observed: NULL or uint64 [P-1][S/chunk_rows]: the 100 MHz device clock
+ *    when the chunk's ready word was seen (0 on time-out).
+ *  - max_workgroups: consumer workgroups, 0 = min(32, chunks).
+ * It may run on another stream while the producer runs; the producer's
+ * workgroups take a whole CU each, so leave the consumer CUs
+ * (pk_options.max_workgroups) or it starts only as producer workgroups end.
+ * Asynchronous; returns PK_OK or PK_ERR_* (arguments checked before any HIP
+ * call). */
+int pk_rs_consume(const uint32_t* flags, const void* send_bufs, void* dest,
+                  int64_t M, int64_t N, int P, int chunk_rows, uint32_t expected,
+                  int spin_limit, int32_t* status, uint64_t* observed,
+                  int max_workgroups, void* stream);
 
 /* Number of uint32 flag words for (P, M, chunk_rows): 2*(P-1)*(M/P)/chunk_rows,
  * or a negative PK_ERR_* code for invalid arguments. */

@@ -75,6 +75,7 @@ __all__ = [
     "gemm_rs_elements",
     "error_bound",
     "OracleResult",
+    "consume_chunks",
 ]
 
 # ---------------------------------------------------------------------------
@@ -331,3 +332,38 @@ def rel_frobenius(a: np.ndarray, ref: np.ndarray) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else math.inf
     return num / den
+
+
+def consume_chunks(ready: np.ndarray, send_bits: np.ndarray, dest_bits: np.ndarray,
+                   chunk_rows: int, expected: int):
+    """The chunk consumer (the step after the share): what dest and the status
+    words hold after one pass.
+
+    [PK] "The Eight PK Primitives": wait spins on a counter until it reaches an
+    expected value; [SYN] 5.1: a chunk moves as one unit.  ``ready`` (uint32
+    [P-1, C]) are the producer's ready words, ``send_bits`` / ``dest_bits``
+    (uint16 [P-1, S, N]) the send buffers and the staging buffers before the
+    pass.  A chunk whose ready word has reached ``expected`` -- compared as a
+    signed 32-bit distance, the reading taken here so that counts may wrap --
+    is copied and gets status 0; any other chunk is left alone and gets
+    status 1 (timed out).  Returns (dest_bits after, status int32 [P-1, C]).
+    """
+    ready = np.asarray(ready, dtype=np.uint32)
+    dest = np.array(dest_bits, dtype=np.uint16, copy=True)
+    n_slots, C = ready.shape
+    if send_bits.shape[0] != n_slots or dest.shape != send_bits.shape:
+        raise ValueError("ready, send and dest disagree on the number of slots")
+    if send_bits.shape[1] != C * chunk_rows:
+        raise ValueError("chunks do not tile the shard")
+    status = np.ones((n_slots, C), dtype=np.int32)
+    for j in range(n_slots):
+        for c in range(C):
+            distance = (int(ready[j, c]) - (expected & 0xFFFFFFFF)) & 0xFFFFFFFF
+            if distance >= 1 << 31:        # as a signed 32-bit value
+                distance -= 1 << 32
+            if distance >= 0:
+                rows = slice(c * chunk_rows, (c + 1) * chunk_rows)
+                dest[j, rows] = send_bits[j, rows]
+                status[j, c] = 0
+    return dest, status
+

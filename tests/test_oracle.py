@@ -473,3 +473,32 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
         monkeypatch.setattr(orc, "bf16_bits_to_f64", lambda b: np.trunc(real(b)))
     with pytest.raises((AssertionError, IndexError)):
         _run_pins()
+
+
+def test_consume_chunks_by_hand():
+    """Worked example: 2 slots x 3 chunks of 2 rows; waits for call 5."""
+    send = np.arange(2 * 6 * 4, dtype=np.uint16).reshape(2, 6, 4)
+    dest = np.full_like(send, 0xFFFF)
+    ready = np.array([[5, 4, 6], [0xFFFFFFFF, 5, 7]], np.uint32)
+    got, status = orc.consume_chunks(ready, send, dest, 2, 5)
+    assert np.array_equal(status, np.array([[0, 1, 0], [1, 0, 0]], np.int32))
+    want = dest.copy()
+    want[0, 0:2] = send[0, 0:2]
+    want[0, 4:6] = send[0, 4:6]
+    want[1, 2:4] = send[1, 2:4]
+    want[1, 4:6] = send[1, 4:6]
+    assert np.array_equal(got, want)
+    assert np.all(dest == 0xFFFF)            # the input is not modified
+
+
+def test_consume_chunks_wraps_at_2_32():
+    send = np.ones((1, 2, 8), np.uint16)
+    dest = np.zeros_like(send)
+    # expected 0xFFFFFFFF: a word that has wrapped to 1 is two calls past it
+    got, status = orc.consume_chunks(np.array([[1, 0xFFFFFFFE]], np.uint32), send, dest, 1,
+                                     0xFFFFFFFF)
+    assert np.array_equal(status, np.array([[0, 1]], np.int32))
+    assert np.array_equal(got[0, 0], send[0, 0]) and np.all(got[0, 1] == 0)
+    with pytest.raises(ValueError):
+        orc.consume_chunks(np.zeros((1, 3), np.uint32), send, dest, 1, 0)
+
