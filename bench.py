@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run 5 device copies of 512 MiB (counter calibration) and exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-consumer", action="store_true",
+                   help="skip the chunk-consumer measurement beside the producer")
     p.add_argument("--no-gemm-only", action="store_true")
     p.add_argument("--sweep", action="store_true",
                    help="large-K schedule sweep: chunk_rows x tile order, one JSON line each")
@@ -147,6 +149,68 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
+    """The chunk consumer beside the producer on the same share.
+
+    The producer runs on CUs - consumer_wgs workgroups.  Timed: the producer
+    alone, then the producer with the consumer on a second stream (copying
+    every chunk into staging buffers as its ready word rises), both as
+    back-to-back repetitions bracketed by events.  Flag latency is the
+    consumer's clock when it saw a word minus the producer's clock when it
+    raised it (100 MHz device clock), over the chunks of the last repetition.
+    """
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = BufferSet(w, 17, w.chunk_rows, torch, gen, pk)
+    n = (w.P - 1) * (w.S // w.chunk_rows)
+    dest = torch.empty_like(s.send)
+    status = torch.zeros(n, dtype=torch.int32, device="cuda")
+    observed = torch.zeros(n, dtype=torch.int64, device="cuda")
+    clock = torch.zeros(n, dtype=torch.int64, device="cuda")
+    out_bf16 = 1 if w.out_dtype == "bf16" else 0
+    sp, sc = torch.cuda.Stream(), torch.cuda.Stream()
+    prod = pk.BoundCall(s.A, s.B, s.peers, s.send, s.out, s.flags, w.M, w.N, w.K, w.P, w.rank,
+                        w.chunk_rows, w.tile_order, out_bf16,
+                        max_workgroups=max(cus - consumer_wgs, 1), ready_clock=clock, stream=sp)
+    calls = 0
+
+    def run(with_consumer, k):
+        nonlocal calls
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(sp)
+        sc.wait_event(t0)
+        for _ in range(k):
+            prod()
+            calls += 1
+            if with_consumer:
+                # consumer n may start before producer call n; it waits for
+                # ready words of n, and the next producer call waits for it
+                # (the send buffers are reused)
+                pk.pk_rs_consume(s.flags, s.send, dest, w.M, w.N, w.P, w.chunk_rows, calls,
+                                 status, observed, spin_limit=1 << 16,
+                                 max_workgroups=consumer_wgs, stream=sc)
+                sp.wait_stream(sc)
+        t1.record(sp)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / k
+
+    run(False, 3)
+    run(True, 3)
+    alone = run(False, reps)
+    both = run(True, reps)
+    st = status.cpu()
+    assert int(st.abs().max()) == 0, "the consumer timed out on a chunk"
+    assert torch.equal(dest.view(torch.int16), s.send.view(torch.int16))
+    lat = ((observed - clock).double() / 100.0).cpu()      # us
+    return {"consumer_workgroups": consumer_wgs, "producer_workgroups": max(cus - consumer_wgs, 1),
+            "producer_alone_us": round(alone * 1e3, 2),
+            "producer_and_consumer_us": round(both * 1e3, 2),
+            "copy_gbps": round(2 * (w.P - 1) * w.S * w.N * 2 / (both * 1e-3) / 1e9, 1),
+            "flag_latency_us": {"median": round(float(lat.median()), 2),
+                                "max": round(float(lat.max()), 2),
+                                "min": round(float(lat.min()), 2)}}
 
 
 def source_digest():
@@ -306,6 +370,8 @@ def main():
             secs.append(sec)
         if secs:
             line["secondary"] = secs[0] if len(secs) == 1 else secs
+    if not args.no_consumer and w.P > 1:
+        line["chunk_consumer"] = measure_consumer(w, args, torch, gen, pk)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gen)
     print(json.dumps(line), flush=True)

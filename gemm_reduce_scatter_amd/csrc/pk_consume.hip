@@ -42,6 +42,7 @@ struct CArgs {
 };
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
 
 __global__ void __launch_bounds__(kThreads) pk_rs_consume_kernel(CArgs a) {
   __shared__ int ok_sh;
@@ -76,7 +77,17 @@ __global__ void __launch_bounds__(kThreads) pk_rs_consume_kernel(CArgs a) {
       const long long base = (long long)j * a.units_per_slot + (long long)c * a.units_per_chunk;
       const u32x4* s = a.src + base;
       u32x4* d = a.dst + base;
-      for (long long u = tid; u < a.units_per_chunk; u += kThreads) d[u] = s[u];
+      // kUnroll loads in flight per thread before their stores: the copy is
+      // bound by bytes in flight per CU, not by instructions
+      long long u = tid;
+      for (; u + (kUnroll - 1) * kThreads < a.units_per_chunk; u += kUnroll * kThreads) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int r = 0; r < kUnroll; ++r) v[r] = __builtin_nontemporal_load(s + u + r * kThreads);
+#pragma unroll
+        for (int r = 0; r < kUnroll; ++r) __builtin_nontemporal_store(v[r], d + u + r * kThreads);
+      }
+      for (; u < a.units_per_chunk; u += kThreads) d[u] = s[u];
     }
     __syncthreads();   // ok_sh is rewritten by the next item
   }
