@@ -579,8 +579,9 @@ struct PeerPrefetch {
 // The peer sum of an owned sub-tile (configuration CO, GS = P-1 slots),
 // accumulated by a workgroup while it multiplies a send tile whose main loop
 // has STEPS k16 steps per trip.  Load g (g = trip*STEPS + step) reads slot
-// g/SEGS of segment g%SEGS; each segment keeps one load in flight and adds
-// it when it issues its next one, SEGS steps later.  The loads go through a
+// g/SEGS of segment g%SEGS; each segment keeps two loads in flight and adds
+// one when it issues the load two slots later, 2*SEGS steps after it was
+// issued, so a load has that many steps of MFMA to land in.  The loads go through a
 // buffer descriptor over the peer partials: slots past P-2 get an offset
 // past its range and read zeros, which add nothing (the sums start at +0
 // and never hold -0).  finish() adds the last loads and any slots a short K
@@ -594,7 +595,7 @@ struct PresumStream {
   static constexpr int LOADS_PER_STEP = 1;
   static_assert(STEPS % SEGS == 0, "whole segments per trip");
   float v[SEGS][8];
-  u32x4 q[SEGS];
+  u32x4 q[2][SEGS];   // slot n of a segment lands in q[n & 1]: two loads in flight
   uint32_t off[SEGS];          // byte offset of each segment in slot 0
   uint32_t slot_bytes;
   __amdgpu_buffer_rsrc_t rsrc;
@@ -620,7 +621,8 @@ struct PresumStream {
     for (int sg = 0; sg < SEGS; ++sg) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[sg][e] = 0.0f;
-      q[sg] = u32x4{0u, 0u, 0u, 0u};
+      q[0][sg] = u32x4{0u, 0u, 0u, 0u};
+      q[1][sg] = u32x4{0u, 0u, 0u, 0u};
     }
     trip = 0;
   }
@@ -633,13 +635,17 @@ struct PresumStream {
   template <int I>
   __device__ __forceinline__ void step(const KArgs&) {
     constexpr int sg = I % SEGS, so = I / SEGS;
-    add_bf16x8(v[sg], q[sg]);                            // the previous slot, or zeros
-    q[sg] = load(off[sg], trip * SPT + so);
+    static_assert(SPT % 2 == 0, "a step's slot parity is the same every trip");
+    add_bf16x8(v[sg], q[so & 1][sg]);                    // slot n-2, or zeros
+    q[so & 1][sg] = load(off[sg], trip * SPT + so);
   }
   __device__ __forceinline__ void end_trip() { ++trip; }
   __device__ __forceinline__ void finish(const KArgs&) {
 #pragma unroll
-    for (int sg = 0; sg < SEGS; ++sg) add_bf16x8(v[sg], q[sg]);
+    for (int sg = 0; sg < SEGS; ++sg) {
+      add_bf16x8(v[sg], q[0][sg]);
+      add_bf16x8(v[sg], q[1][sg]);
+    }
     for (int slot = trip * SPT; slot < GS; ++slot)
 #pragma unroll
       for (int sg = 0; sg < SEGS; ++sg) add_bf16x8(v[sg], load(off[sg], slot));
