@@ -78,6 +78,9 @@ def load():
     lib.pk_rs_consume.argtypes = [vp, vp, vp, i64, i64, i32, i32, ctypes.c_uint32, i32, vp, vp,
                                   i32, vp]
     lib.pk_rs_consume.restype = i32
+    lib.pk_gemm_rs_push.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
+                                    ctypes.POINTER(_Options), vp]
+    lib.pk_gemm_rs_push.restype = i32
     del u32p
     _lib = lib
     return lib
@@ -217,6 +220,32 @@ def _check_clock(ready_clock, M, P, chunk_rows, gemm_only=False):
         raise ValueError("ready_clock must be a contiguous 64-bit device tensor")
     if ready_clock.numel() < _chunks(M, P, chunk_rows):
         raise ValueError("ready_clock needs one word per chunk")
+
+
+def pk_gemm_rs_push(A, B, accum, flags, M, N, K, P, rank, chunk_rows, tile_order, config=0,
+                    max_workgroups=0, group_n=0, signal_batch=0, ready_clock=None,
+                    stream=None) -> int:
+    """Atomic push variant: accum[d] += this rank's partial rows of shard d for
+    every owner d (fp32 atomics); see pk_gemm_rs.h."""
+    import torch
+    _check_tensors(A, B, None, None, accum, flags)
+    if accum.dtype != torch.float32:
+        raise ValueError("accum must be float32")
+    M_, N_, K_, P_ = int(M), int(N), int(K), int(P)
+    if P_ >= 1 and M_ > 0 and N_ > 0 and K_ >= 0 and M_ % P_ == 0:
+        need = [("A", A, 2 * M_ * K_), ("B", B, 2 * K_ * N_), ("accum", accum, 4 * M_ * N_)]
+        words = load().pk_flags_words(P_, M_, int(chunk_rows))
+        if words >= 0:
+            need.append(("flags", flags, 4 * words))
+        for name, t, nbytes in need:
+            if t is not None and t.numel() * t.element_size() < nbytes:
+                raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, "
+                                 f"the call needs {nbytes}")
+    _check_clock(ready_clock, M, P, chunk_rows)
+    o = _opts(config, max_workgroups, group_n, False, 0, signal_batch, ready_clock)
+    return _check(load().pk_gemm_rs_push(
+        _ptr(A), _ptr(B), _ptr(accum), _ptr(flags), M_, N_, K_, P_, int(rank), int(chunk_rows),
+        int(tile_order), ctypes.byref(o), _stream(stream)))
 
 
 def pk_rs_consume(flags, send_bufs, dest, M, N, P, chunk_rows, expected, status,

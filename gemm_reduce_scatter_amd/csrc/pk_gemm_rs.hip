@@ -496,7 +496,10 @@ __device__ __forceinline__ void signal_batch(const KArgs& a, long long fk, long 
   }
 }
 
-enum Mode : int { kFused = 0, kGemmOnly = 1 };
+// kFused: staged reduce-scatter (send chunks + owner-side sum of the staged
+// peer partials); kGemmOnly: plain GEMM; kPush: every tile added with fp32
+// atomics into the accumulator of the rank that owns its rows.
+enum Mode : int { kFused = 0, kGemmOnly = 1, kPush = 2 };
 
 // ---------------------------------------------------------------------------
 // Epilogue of one work item.  Each wave re-lays its accumulators, one 16-row
@@ -699,7 +702,26 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
           stage[row * C::EPI_STRIDE + fn * 32 + (lane & 31)] = acc[fm][fn][r];
         }
       wave_lds_sync();
-      if (!owned) {
+      if (MODE == kPush) {
+        // out holds the P owners' fp32 accumulators, [P][S][N]
+        float* accum = reinterpret_cast<float*>(a.out) + (long long)shard * slot_stride;
+#pragma unroll
+        for (int it = 0; it < PASSES; ++it) {
+          const int rr = it * RPI + lane / LPR;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
+          const int lr = lrow0 + SG::row(wm, lane, fm, h, it);
+          if (lr < a.S && col_ok) {
+            float* dst = accum + (long long)lr * a.N + col;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              __hip_atomic_fetch_add(dst + e, x0[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_fetch_add(dst + 4 + e, x1[e], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      } else if (!owned) {
 #pragma unroll
         for (int it = 0; it < PASSES; ++it) {
           const int rr = it * RPI + lane / LPR;
@@ -934,8 +956,8 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       const TileCoord tc = tile_at(a.g, s);
       process<CS, MODE, GS, kPeersDirect>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1,
                                           lds2, lds3, tid, wave, lane, nobg, nopv);
-      if (MODE == kFused && tc.shard != a.rank) ++npend;
-      if (MODE == kFused && npend > 0 && (npend >= a.sig_batch || last)) flush(k);
+      if (MODE != kGemmOnly && tc.shard != a.rank) ++npend;
+      if (MODE != kGemmOnly && npend > 0 && (npend >= a.sig_batch || last)) flush(k);
     } else {
       const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
       if (s < n_send) {
@@ -1054,6 +1076,28 @@ static int validate(const void* A, const void* B, const void* peers, const void*
   return PK_OK;
 }
 
+// Arguments of the atomic push variant: `out` is the owners' fp32
+// accumulators [P][S][N]; no peers or send buffers; gemm_only and the owned
+// split do not apply.
+static int validate_push(const void* A, const void* B, const void* accum, const uint32_t* flags,
+                         long long M, long long N, long long K, int P, int rank, int chunk_rows,
+                         int tile_order, const pk_options* o) {
+  if (o && (o->gemm_only != 0 || o->owned_split == 1)) return PK_ERR_CONFIG;
+  // the shape, rank, order and option checks of the staged variant; its
+  // pointer checks ask for peers and send buffers, so they are redone here
+  const int v = validate(A, B, nullptr, nullptr, accum, flags, M, N, K, P, rank, chunk_rows,
+                         tile_order, 0, o);
+  if (v != PK_OK && v != PK_ERR_POINTER) return v;
+  if (M == 0 || N == 0) return PK_OK;
+  auto a16 = [](const void* p) { return p != nullptr && aligned16(p); };
+  if (!a16(accum) || (K > 0 && (!a16(A) || !a16(B)))) return PK_ERR_POINTER;
+  if (P > 1 && (flags == nullptr || (reinterpret_cast<uintptr_t>(flags) & 3u)))
+    return PK_ERR_POINTER;
+  if (o && o->ready_clock && (reinterpret_cast<uintptr_t>(o->ready_clock) & 7u))
+    return PK_ERR_POINTER;
+  return PK_OK;
+}
+
 // Resident workgroups per CU of one kernel instance, asked once per device.
 template <class CS, class CO, int MODE, int GS>
 static int occupancy_of(int dev) {
@@ -1112,14 +1156,15 @@ static bool use_owned_split(int cfg, int P, long long S, long long N, long long 
 }
 
 template <class C>
-static int launch(KArgs& a, bool gemm_only, int cfg, const pk_options* o, hipStream_t stream) {
+static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t stream) {
+  const bool gemm_only = mode == kGemmOnly;
   a.g.BM = C::BM;
   a.g.BN = C::BN;
   a.g.Tm = a.S > 0 ? ceil_div(a.S, C::BM) : 0;
   a.g.Tn = ceil_div(a.N, C::BN);
   a.g.group_n = (o && o->group_n > 0) ? o->group_n : default_group_n(kCfgs[0], a.g.Tn);
   a.g.Rm = a.g.Rn = 1;
-  const bool split = !gemm_only && use_owned_split(cfg, a.P, a.S, a.N, a.g.total(), o);
+  const bool split = mode == kFused && use_owned_split(cfg, a.P, a.S, a.N, a.g.total(), o);
   if (split) {
     a.g.Rm = C::BM / CfgOwned::BM;
     a.g.Rn = C::BN / CfgOwned::BN;
@@ -1127,6 +1172,7 @@ static int launch(KArgs& a, bool gemm_only, int cfg, const pk_options* o, hipStr
   a.total_tiles = split ? split_pairs(a.g) : a.g.total();
   if (a.total_tiles == 0) return PK_OK;
   if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
+  if (mode == kPush) return launch_as<C, C, kPush, 1>(a, o, stream);
   if constexpr (__is_same(C, Cfg1)) {
     if (split) {
       switch (a.P - 1) {
@@ -1145,9 +1191,11 @@ static int launch(KArgs& a, bool gemm_only, int cfg, const pk_options* o, hipStr
 
 static int run(const void* A, const void* B, const void* peers, void* send, void* out,
                uint32_t* flags, long long M, long long N, long long K, int P, int rank,
-               int chunk_rows, int tile_order, int out_bf16, const pk_options* o, void* stream) {
-  const int v = validate(A, B, peers, send, out, flags, M, N, K, P, rank, chunk_rows, tile_order,
-                         out_bf16, o);
+               int chunk_rows, int tile_order, int out_bf16, const pk_options* o, void* stream,
+               bool push = false) {
+  const int v = push ? validate_push(A, B, out, flags, M, N, K, P, rank, chunk_rows, tile_order, o)
+                     : validate(A, B, peers, send, out, flags, M, N, K, P, rank, chunk_rows,
+                                tile_order, out_bf16, o);
   if (v != PK_OK) return v;
   if (M == 0 || N == 0) return PK_OK;
   KArgs a;
@@ -1160,7 +1208,8 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.M = M;
   a.N = (int)N;
   a.K = (int)K;
-  const bool gemm_only = o && o->gemm_only;
+  const bool gemm_only = !push && o && o->gemm_only;
+  const int mode = push ? kPush : gemm_only ? kGemmOnly : kFused;
   if (gemm_only) {
     // One shard covering every row, nothing sent.
     a.P = 1;
@@ -1187,11 +1236,11 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg) {
-    case 1: return launch<Cfg1>(a, gemm_only, cfg, o, s);
-    case 2: return launch<Cfg2>(a, gemm_only, cfg, o, s);
-    case 3: return launch<Cfg3>(a, gemm_only, cfg, o, s);
-    case 4: return launch<Cfg4>(a, gemm_only, cfg, o, s);
-    case 5: return launch<Cfg5>(a, gemm_only, cfg, o, s);
+    case 1: return launch<Cfg1>(a, mode, cfg, o, s);
+    case 2: return launch<Cfg2>(a, mode, cfg, o, s);
+    case 3: return launch<Cfg3>(a, mode, cfg, o, s);
+    case 4: return launch<Cfg4>(a, mode, cfg, o, s);
+    case 5: return launch<Cfg5>(a, mode, cfg, o, s);
     default: return PK_ERR_CONFIG;
   }
 }
@@ -1224,6 +1273,13 @@ int pk_gemm_rs_local_ex(const void* A, const void* B, const void* peer_partials,
                         const pk_options* opts, void* stream) {
   return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
                  tile_order, out_bf16, opts, stream);
+}
+
+int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags, int64_t M,
+                    int64_t N, int64_t K, int P, int rank, int chunk_rows, int tile_order,
+                    const pk_options* opts, void* stream) {
+  return pk::run(A, B, nullptr, nullptr, accum, flags, M, N, K, P, rank, chunk_rows, tile_order,
+                 0, opts, stream, true);
 }
 
 int64_t pk_flags_words(int P, int64_t M, int chunk_rows) {

@@ -120,6 +120,26 @@ int pk_gemm_rs_local_ex(const void* A, const void* B, const void* peer_partials,
                         int chunk_rows, int tile_order, int out_bf16,
                         const pk_options* opts, void* stream);
 
+/* Atomic push variant: the pages' own epilogue ("The Eight PK Primitives" of
+ * the ParallelKittens summary page: store_add_async adds a tile atomically
+ * into a peer's buffer; section 3 "Scheduling Analysis" sends every output
+ * tile to its owner that way).  Every tile of this rank's partial
+ * C_loc = A * B is added, element by element with fp32 atomic adds, into the
+ * accumulator of the rank that owns its rows:
+ *   accum[d] += C_loc rows of shard d      for every d in 0..P-1 (own shard too)
+ * accum: fp32 [P][S][N], 16-byte aligned: accum[d] stands for rank d's
+ * accumulator (on one GPU, a local buffer); what it holds before the call
+ * (other ranks' contributions, or zeros) is what the adds land on.  Each
+ * element receives one add per call, so the result is fl32(before + C_loc)
+ * whatever the tile order.  Ready words as for pk_gemm_rs_local: for the P-1
+ * other owners, a chunk's word rises by one once this rank's adds into it
+ * are complete and visible at device scope.  No peer partials, no send
+ * buffers.  opts: config, max_workgroups, group_n, signal_batch and
+ * ready_clock apply; gemm_only and owned_split = 1 are PK_ERR_CONFIG. */
+int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags,
+                    int64_t M, int64_t N, int64_t K, int P, int rank,
+                    int chunk_rows, int tile_order, const pk_options* opts, void* stream);
+
 /* Chunk consumer: the transfer half of the reduce-scatter, the step after
  * the fused share ("The Eight PK Primitives" of the ParallelKittens summary
  * page: wait spins on a counter until it reaches an expected value; chunks

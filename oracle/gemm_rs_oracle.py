@@ -76,6 +76,7 @@ __all__ = [
     "error_bound",
     "OracleResult",
     "consume_chunks",
+    "push_share",
 ]
 
 # ---------------------------------------------------------------------------
@@ -366,4 +367,39 @@ def consume_chunks(ready: np.ndarray, send_bits: np.ndarray, dest_bits: np.ndarr
                 dest[j, rows] = send_bits[j, rows]
                 status[j, c] = 0
     return dest, status
+
+
+def push_share(C: np.ndarray, accum_before: np.ndarray, P: int, rank: int, chunk_rows: int,
+               ready_before=None):
+    """Atomic push variant: what one rank's share leaves in the owners'
+    accumulators.
+
+    [PK] "The Eight PK Primitives": store_add_async adds a tile atomically
+    into a peer's buffer; [PK] "Scheduling Analysis": each output tile goes to
+    the rank that owns its rows.  ``accum_before`` (float64 [P, S, N]) holds
+    the owners' accumulators before the call; every owner d (this rank
+    included) receives this rank's partial rows of shard d once:
+    accum[d] = accum_before[d] + C[d*S:(d+1)*S], exact in fp64.  Ready words
+    and counters as in reduce_scatter_share: each of the P-1 other owners'
+    chunks is signalled once.  Returns (accum float64 [P, S, N], ready,
+    counters).
+    """
+    M, N = C.shape
+    if P < 1 or not (0 <= rank < P) or M % P:
+        raise ValueError("need P >= 1, 0 <= rank < P and P dividing M")
+    S = M // P
+    accum_before = np.asarray(accum_before, dtype=np.float64)
+    if accum_before.shape != (P, S, N):
+        raise ValueError(f"accum_before must have shape {(P, S, N)}")
+    accum = accum_before.copy()
+    for d in range(P):
+        accum[d] = accum[d] + C[d * S:(d + 1) * S, :]
+    if chunk_rows <= 0 or S % chunk_rows:
+        raise ValueError("chunk_rows must divide the shard height")
+    n_chunks = S // chunk_rows
+    if ready_before is None:
+        ready_before = np.zeros((P - 1, n_chunks), dtype=np.uint32)
+    ready = np.asarray(ready_before, dtype=np.uint32) + np.uint32(1)
+    counters = np.zeros((P - 1, n_chunks), dtype=np.uint32)
+    return accum, ready, counters
 

@@ -502,3 +502,42 @@ def test_consume_chunks_wraps_at_2_32():
     with pytest.raises(ValueError):
         orc.consume_chunks(np.zeros((1, 3), np.uint32), send, dest, 1, 0)
 
+
+def test_push_share_matches_the_staged_share():
+    """Owner's accumulator pre-filled with the peers' sum: the push result on
+    the owned shard is the staged owned sum, the other owners get C's rows."""
+    rng = np.random.default_rng(6)
+    P, rank, M, K, N, cr = 4, 1, 32, 6, 8, 4
+    S = M // P
+    A, B = _int_mats(rng, M, K, N)
+    peers = rng.integers(-8, 9, (P - 1, S, N)).astype(np.float64)
+    C = A.astype(np.float64) @ B.astype(np.float64)
+    staged = orc.reduce_scatter_share(C, peers, P, rank, cr)
+    before = np.zeros((P, S, N))
+    before[rank] = peers.sum(axis=0)
+    acc, ready, counters = orc.push_share(C, before, P, rank, cr)
+    assert np.array_equal(acc[rank], staged.out)
+    for d in range(P):
+        if d != rank:
+            assert np.array_equal(acc[d], C[d * S:(d + 1) * S])
+    assert np.array_equal(ready, staged.ready) and np.array_equal(counters, staged.counters)
+
+
+def test_push_from_every_rank_gives_the_full_sum():
+    """P ranks pushing into shared accumulators: accumulator d ends with
+    sum_p A_p . B_p restricted to shard d (the reduce-scatter's definition)."""
+    rng = np.random.default_rng(7)
+    P, M, K, N = 3, 12, 5, 4
+    S = M // P
+    acc = np.zeros((P, S, N))
+    full = np.zeros((M, N))
+    for r in range(P):
+        A, B = _int_mats(rng, M, K, N)
+        C = A.astype(np.float64) @ B.astype(np.float64)
+        full += C
+        acc, _, _ = orc.push_share(C, acc, P, r, 2)
+    for d in range(P):
+        assert np.array_equal(acc[d], full[d * S:(d + 1) * S])
+    with pytest.raises(ValueError):
+        orc.push_share(np.zeros((12, 4)), np.zeros((2, 4, 4)), 3, 0, 2)
+
