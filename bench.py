@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run 5 device copies of 512 MiB (counter calibration) and exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-push", action="store_true",
+                   help="skip the atomic push variant beside the staged share")
     p.add_argument("--no-consumer", action="store_true",
                    help="skip the chunk-consumer measurement beside the producer")
     p.add_argument("--no-gemm-only", action="store_true")
@@ -149,6 +151,21 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def measure_push(w, args, torch, gen, pk, steps, warmup):
+    """The atomic push variant on the same share: fp32 atomic adds of every
+    tile into the owners' accumulators [P][S][N], timed like the staged
+    share (back-to-back launches, events over the region)."""
+    s = BufferSet(w, 17, w.chunk_rows, torch, gen, pk)
+    accum = torch.zeros((w.P, w.S, w.N), dtype=torch.float32, device="cuda")
+    call = pk.BoundPush(s.A, s.B, accum, s.flags, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
+                        w.tile_order)
+    ms, _ = time_steps(lambda i: call(), 1, warmup, steps, torch)
+    # bytes the adds move: every accumulator word read and written once
+    rmw = 2 * 4 * w.M * w.N
+    return {"kernel_ms": round(ms, 5), "accum_rmw_bytes": rmw,
+            "accum_rmw_gbps": round(rmw / (ms * 1e-3) / 1e9, 1)}
 
 
 def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
@@ -367,9 +384,16 @@ def main():
             if "gemm_only_kernel_ms" in r2:
                 sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
                 sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
+            if not args.no_push:
+                pu = measure_push(w2, args, torch, gen, pk, max(5, args.steps // 5), 3)
+                sec["atomic_push_kernel_ms"] = pu["kernel_ms"]
             secs.append(sec)
         if secs:
             line["secondary"] = secs[0] if len(secs) == 1 else secs
+    if not args.no_push:
+        pu = measure_push(w, args, torch, gen, pk, args.steps, args.warmup)
+        pu["vs_staged"] = round(pu["kernel_ms"] / r["kernel_ms"], 3)
+        line["atomic_push"] = pu
     if not args.no_consumer and w.P > 1:
         line["chunk_consumer"] = measure_consumer(w, args, torch, gen, pk)
     if not args.no_cpu_baseline:

@@ -248,6 +248,27 @@ def pk_gemm_rs_push(A, B, accum, flags, M, N, K, P, rank, chunk_rows, tile_order
         int(tile_order), ctypes.byref(o), _stream(stream)))
 
 
+class BoundPush:
+    """pk_gemm_rs_push with its arguments checked and marshalled once; calling
+    the object launches it again (see BoundCall)."""
+
+    def __init__(self, A, B, accum, flags, M, N, K, P, rank, chunk_rows, tile_order, config=0,
+                 max_workgroups=0, group_n=0, signal_batch=0, stream=None):
+        import torch
+        _check_tensors(A, B, None, None, accum, flags)
+        if accum.dtype != torch.float32 or accum.numel() < int(M) * int(N):
+            raise ValueError("accum must be float32 [P][S][N]")
+        self._keep = (A, B, accum, flags)
+        self._opts = _opts(config, max_workgroups, group_n, False, 0, signal_batch)
+        self._fn = load().pk_gemm_rs_push
+        self._args = (_ptr(A), _ptr(B), _ptr(accum), _ptr(flags), int(M), int(N), int(K),
+                      int(P), int(rank), int(chunk_rows), int(tile_order),
+                      ctypes.byref(self._opts), _stream(stream))
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._args))
+
+
 def pk_rs_consume(flags, send_bufs, dest, M, N, P, chunk_rows, expected, status,
                   observed=None, spin_limit=1 << 16, max_workgroups=0, stream=None) -> int:
     """Chunk consumer: wait for each chunk's ready word to reach `expected`,
