@@ -81,6 +81,9 @@ def load():
     lib.pk_gemm_rs_push.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32,
                                     ctypes.POINTER(_Options), vp]
     lib.pk_gemm_rs_push.restype = i32
+    lib.pk_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32,
+                               ctypes.c_uint32, i32, i32, ctypes.POINTER(_Options), vp]
+    lib.pk_ag_gemm.restype = i32
     del u32p
     _lib = lib
     return lib
@@ -264,6 +267,62 @@ class BoundPush:
         self._args = (_ptr(A), _ptr(B), _ptr(accum), _ptr(flags), int(M), int(N), int(K),
                       int(P), int(rank), int(chunk_rows), int(tile_order),
                       ctypes.byref(self._opts), _stream(stream))
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._args))
+
+
+def _ag_args(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows):
+    import torch
+    for name, t in (("A", A), ("B", B), ("C", C), ("a_ready", a_ready), ("error", error)):
+        if t is None:
+            if int(P) > 1 and name in ("a_ready", "error"):
+                raise ValueError(f"{name} is required when P > 1")
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    M_, N_, K_, P_ = int(M), int(N), int(K), int(P)
+    if P_ >= 1 and M_ > 0 and N_ > 0 and K_ >= 0 and M_ % P_ == 0:
+        need = [("A", A, 2 * M_ * K_), ("B", B, 2 * K_ * N_), ("C", C, 2 * M_ * N_)]
+        S = M_ // P_
+        if P_ > 1 and int(chunk_rows) > 0 and S % int(chunk_rows) == 0:
+            need.append(("a_ready", a_ready, 4 * P_ * (S // int(chunk_rows))))
+        for name, t, nbytes in need:
+            if t is not None and t.numel() * t.element_size() < nbytes:
+                raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, "
+                                 f"the call needs {nbytes}")
+
+
+def pk_ag_gemm(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows, expected,
+               spin_limit=1 << 16, tile_order=1, config=0, max_workgroups=0, group_n=0,
+               stream=None) -> int:
+    """All-gather + GEMM: C = A_gathered * B, each tile of another rank's rows
+    waiting for its A chunks' ready words (see pk_gemm_rs.h)."""
+    _ag_args(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows)
+    o = _opts(config, max_workgroups, group_n)
+    return _check(load().pk_ag_gemm(
+        _ptr(A), _ptr(a_ready), _ptr(B), _ptr(C), _ptr(error), int(M), int(N), int(K), int(P),
+        int(rank), int(chunk_rows), ctypes.c_uint32(int(expected) & 0xFFFFFFFF),
+        int(spin_limit), int(tile_order), ctypes.byref(o), _stream(stream)))
+
+
+class BoundAgGemm:
+    """pk_ag_gemm with its arguments checked and marshalled once (see BoundCall)."""
+
+    def __init__(self, A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows, expected,
+                 spin_limit=1 << 16, tile_order=1, config=0, max_workgroups=0, group_n=0,
+                 stream=None):
+        _ag_args(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows)
+        self._keep = (A, a_ready, B, C, error)
+        self._opts = _opts(config, max_workgroups, group_n)
+        self._fn = load().pk_ag_gemm
+        self._args = (_ptr(A), _ptr(a_ready), _ptr(B), _ptr(C), _ptr(error), int(M), int(N),
+                      int(K), int(P), int(rank), int(chunk_rows),
+                      ctypes.c_uint32(int(expected) & 0xFFFFFFFF), int(spin_limit),
+                      int(tile_order), ctypes.byref(self._opts), _stream(stream))
 
     def __call__(self) -> int:
         return _check(self._fn(*self._args))

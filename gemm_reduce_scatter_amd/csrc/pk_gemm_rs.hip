@@ -112,6 +112,13 @@ struct KArgs {
   int out_bf16;
   int sig_batch;       // send tiles per ready-word release (>= 1)
   uint64_t* ready_clock;   // null, or [P-1][n_chunks]: device clock when a ready word rose
+  // all-gather + GEMM: ready words [P][n_chunks] of the gathered A rows, the
+  // value that means "arrived", polls per word before giving up, and the
+  // word set to 1 when a wait gave up
+  const uint32_t* wait_ready;
+  uint32_t wait_expected;
+  int spin_limit;
+  int32_t* wait_error;
   Grid g;
   long long total_tiles;
 };
@@ -498,8 +505,10 @@ __device__ __forceinline__ void signal_batch(const KArgs& a, long long fk, long 
 
 // kFused: staged reduce-scatter (send chunks + owner-side sum of the staged
 // peer partials); kGemmOnly: plain GEMM; kPush: every tile added with fp32
-// atomics into the accumulator of the rank that owns its rows.
-enum Mode : int { kFused = 0, kGemmOnly = 1, kPush = 2 };
+// atomics into the accumulator of the rank that owns its rows; kAgGemm:
+// all-gather + GEMM, a tile of another rank's rows first waits for the
+// ready words of the A chunks it reads.
+enum Mode : int { kFused = 0, kGemmOnly = 1, kPush = 2, kAgGemm = 3 };
 
 // ---------------------------------------------------------------------------
 // Epilogue of one work item.  Each wave re-lays its accumulators, one 16-row
@@ -732,7 +741,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
             const u32x4 o = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
                              pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
             uint16_t* dst;
-            if (MODE == kGemmOnly)
+            if (MODE == kGemmOnly || MODE == kAgGemm)
               dst = reinterpret_cast<uint16_t*>(a.out) + ((long long)shard * a.S + lr) * a.N + col;
             else
               dst = a.send + (slot * (long long)a.S + lr) * a.N + col;
@@ -891,6 +900,36 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
 // background, sends, then multiplies the sub-tile and adds that sum.
 // Positions past the end of one list hold only the other (a lone sub-tile
 // reads its peer partials ahead into registers).
+// All-gather + GEMM: before a tile of rank tc.shard's rows reads A, one
+// thread waits (the pages' wait primitive) until the ready word of every A
+// chunk the tile's rows touch has reached wait_expected, a signed 32-bit
+// distance so counts may wrap, polling each at most spin_limit times; every
+// wave then acquires, so the loads of the tile see the chunk data.  A wait
+// that gives up sets *wait_error and the tile is computed from whatever the
+// rows hold, so a missing producer ends the kernel instead of hanging it.
+__device__ __forceinline__ void wait_rows(const KArgs& a, const TileCoord& tc, int BM, int tid) {
+  if (tid == 0) {
+    int c0, c1;
+    chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
+    bool all = true;
+    for (int c = c0; c <= c1; ++c) {
+      const uint32_t* w = a.wait_ready + (long long)tc.shard * a.n_chunks + c;
+      int polls = 0;
+      while ((int32_t)(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       a.wait_expected) < 0) {
+        if (++polls >= a.spin_limit) {
+          all = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!all) __hip_atomic_store(a.wait_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 template <class CS, class CO, int MODE, int GS>
 __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   using L = LdsPlan<CS, CO>;
@@ -954,10 +993,14 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
     const bool last = pos(k + 1) >= a.total_tiles;
     if constexpr (!SPLIT) {
       const TileCoord tc = tile_at(a.g, s);
+      if constexpr (MODE == kAgGemm) {
+        if (tc.shard != a.rank) wait_rows(a, tc, CS::BM, tid);
+      }
       process<CS, MODE, GS, kPeersDirect>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1,
                                           lds2, lds3, tid, wave, lane, nobg, nopv);
-      if (MODE != kGemmOnly && tc.shard != a.rank) ++npend;
-      if (MODE != kGemmOnly && npend > 0 && (npend >= a.sig_batch || last)) flush(k);
+      if ((MODE == kFused || MODE == kPush) && tc.shard != a.rank) ++npend;
+      if ((MODE == kFused || MODE == kPush) && npend > 0 && (npend >= a.sig_batch || last))
+        flush(k);
     } else {
       const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
       if (s < n_send) {
@@ -1173,6 +1216,7 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
   if (a.total_tiles == 0) return PK_OK;
   if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
   if (mode == kPush) return launch_as<C, C, kPush, 1>(a, o, stream);
+  if (mode == kAgGemm) return launch_as<C, C, kAgGemm, 1>(a, o, stream);
   if constexpr (__is_same(C, Cfg1)) {
     if (split) {
       switch (a.P - 1) {
@@ -1233,6 +1277,10 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.g.order = tile_order;
   a.sig_batch = (o && o->signal_batch > 0) ? o->signal_batch : kDefaultSignalBatch;
   a.ready_clock = o ? o->ready_clock : nullptr;
+  a.wait_ready = nullptr;
+  a.wait_expected = 0;
+  a.spin_limit = 1;
+  a.wait_error = nullptr;
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg) {
@@ -1241,6 +1289,61 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
     case 3: return launch<Cfg3>(a, mode, cfg, o, s);
     case 4: return launch<Cfg4>(a, mode, cfg, o, s);
     case 5: return launch<Cfg5>(a, mode, cfg, o, s);
+    default: return PK_ERR_CONFIG;
+  }
+}
+
+// All-gather + GEMM: C [M][N] bf16 = A [M][K] (gathered rows) * B [K][N].
+static int run_ag(const void* A, const uint32_t* a_ready, const void* B, void* Cout,
+                  int32_t* error, long long M, long long N, long long K, int P, int rank,
+                  int chunk_rows, uint32_t expected, int spin_limit, int tile_order,
+                  const pk_options* o, void* stream) {
+  if (P < 1 || P > 64 || rank < 0 || rank >= P) return PK_ERR_RANK;
+  if (tile_order < 0 || tile_order > 2) return PK_ERR_TILE_ORDER;
+  if (M < 0 || N < 0 || K < 0 || M % P != 0 || N % 8 != 0 || K % 8 != 0) return PK_ERR_SHAPE;
+  const long long S = M / P;
+  if (S > 0 && (chunk_rows <= 0 || S % chunk_rows != 0)) return PK_ERR_SHAPE;
+  if (M > (1LL << 31) || N > kMaxN || K > kMaxK) return PK_ERR_TOO_LARGE;
+  if (spin_limit < 1) return PK_ERR_CONFIG;
+  if (o && (o->config < 0 || o->config > kNumCfgs || o->max_workgroups < 0 || o->group_n < 0 ||
+            o->gemm_only != 0 || o->owned_split == 1 || o->signal_batch < 0))
+    return PK_ERR_CONFIG;
+  if (M == 0 || N == 0) return PK_OK;
+  if (!aligned16(Cout) || (K > 0 && (!aligned16(A) || !aligned16(B)))) return PK_ERR_POINTER;
+  if (P > 1 && (a_ready == nullptr || (reinterpret_cast<uintptr_t>(a_ready) & 3u) ||
+                error == nullptr || (reinterpret_cast<uintptr_t>(error) & 3u)))
+    return PK_ERR_POINTER;
+  KArgs a{};
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.out = Cout;
+  a.M = M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.P = P;
+  a.rank = rank;
+  a.S = (int)S;
+  a.chunk_rows = chunk_rows > 0 ? chunk_rows : 1;
+  a.n_chunks = chunk_rows > 0 ? (int)(S / chunk_rows) : 0;
+  a.out_bf16 = 1;
+  a.sig_batch = 1;
+  a.wait_ready = a_ready;
+  a.wait_expected = expected;
+  a.spin_limit = spin_limit;
+  a.wait_error = error;
+  a.g.P = P;
+  a.g.rank = rank;
+  a.g.S = (int)S;
+  a.g.N = (int)N;
+  a.g.order = tile_order;
+  const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, P);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (cfg) {
+    case 1: return launch<Cfg1>(a, kAgGemm, cfg, o, s);
+    case 2: return launch<Cfg2>(a, kAgGemm, cfg, o, s);
+    case 3: return launch<Cfg3>(a, kAgGemm, cfg, o, s);
+    case 4: return launch<Cfg4>(a, kAgGemm, cfg, o, s);
+    case 5: return launch<Cfg5>(a, kAgGemm, cfg, o, s);
     default: return PK_ERR_CONFIG;
   }
 }
@@ -1280,6 +1383,14 @@ int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags,
                     const pk_options* opts, void* stream) {
   return pk::run(A, B, nullptr, nullptr, accum, flags, M, N, K, P, rank, chunk_rows, tile_order,
                  0, opts, stream, true);
+}
+
+int pk_ag_gemm(const void* A, const uint32_t* a_ready, const void* B, void* C, int32_t* error,
+               int64_t M, int64_t N, int64_t K, int P, int rank, int chunk_rows,
+               uint32_t expected, int spin_limit, int tile_order, const pk_options* opts,
+               void* stream) {
+  return pk::run_ag(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows, expected, spin_limit,
+                    tile_order, opts, stream);
 }
 
 int64_t pk_flags_words(int P, int64_t M, int chunk_rows) {

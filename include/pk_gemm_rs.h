@@ -140,6 +140,31 @@ int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags,
                     int64_t M, int64_t N, int64_t K, int P, int rank,
                     int chunk_rows, int tile_order, const pk_options* opts, void* stream);
 
+/* All-gather + GEMM, the step before the reduce-scatter in a tensor-
+ * parallel MLP (ParallelKittens summary page, "Data and Tensor Parallelism:
+ * AG+GEMM, GEMM+RS, and GEMM+AR": local shape N x N/8 x N; Syncopate's
+ * AG-GEMM).  Rank p holds rows [p*S, (p+1)*S) of A (S = M/P); the others'
+ * rows arrive chunk by chunk into the gathered buffer:
+ *   C = A * B,  A: bf16 [M][K] (gathered; this rank's rows already in place),
+ *   B: bf16 [K][N] (this rank's columns), C: bf16 [M][N] (fp32 accumulation,
+ *   rounded to nearest even once).
+ * a_ready: uint32 [P][S/chunk_rows]; word (p, c) counts the arrivals of rows
+ * [c*chunk_rows, (c+1)*chunk_rows) of rank p's shard (this rank's words are
+ * not read).  Before a tile of rank p's rows reads A it waits (the pages'
+ * wait primitive) until every chunk word its rows touch has reached
+ * `expected` (signed 32-bit distance, so counts may wrap), polling each at
+ * most spin_limit >= 1 times, then acquires at device scope.  A wait that
+ * gives up sets *error to 1 (int32, device memory; the caller zeroes it) and
+ * the tile is computed from whatever the rows hold.  tile_order as for the
+ * fused share: PK_TILE_OWNED_FIRST multiplies this rank's own rows first,
+ * then ranks rank+1, rank+2, ... in ring order.  opts: config,
+ * max_workgroups and group_n apply (leave CUs to whatever produces the
+ * chunks if it runs on the same GPU). */
+int pk_ag_gemm(const void* A, const uint32_t* a_ready, const void* B, void* C, int32_t* error,
+               int64_t M, int64_t N, int64_t K, int P, int rank, int chunk_rows,
+               uint32_t expected, int spin_limit, int tile_order, const pk_options* opts,
+               void* stream);
+
 /* Chunk consumer: the transfer half of the reduce-scatter, the step after
  * the fused share ("The Eight PK Primitives" of the ParallelKittens summary
  * page: wait spins on a counter until it reaches an expected value; chunks

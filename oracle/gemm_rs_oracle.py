@@ -77,6 +77,7 @@ __all__ = [
     "OracleResult",
     "consume_chunks",
     "push_share",
+    "ag_gemm",
 ]
 
 # ---------------------------------------------------------------------------
@@ -402,4 +403,37 @@ def push_share(C: np.ndarray, accum_before: np.ndarray, P: int, rank: int, chunk
     ready = np.asarray(ready_before, dtype=np.uint32) + np.uint32(1)
     counters = np.zeros((P - 1, n_chunks), dtype=np.uint32)
     return accum, ready, counters
+
+
+def ag_gemm(A_bits: np.ndarray, B_bits: np.ndarray, ready: np.ndarray, P: int, rank: int,
+            chunk_rows: int, expected: int):
+    """All-gather + GEMM, the step before the share in a tensor-parallel MLP.
+
+    [PK] "Data and Tensor Parallelism: AG+GEMM, GEMM+RS, and GEMM+AR": the
+    rows of A are gathered from the P ranks (rank p owns rows [p*S, (p+1)*S))
+    and multiplied by this rank's B.  ``A_bits`` (uint16 [M, K]) is the
+    gathered buffer, ``ready`` (uint32 [P, S/chunk_rows]) the arrival words of
+    its chunks.  Returns (C float64 [M, N] = A . B exactly, error) where error
+    is 1 when some chunk of another rank's rows has not reached ``expected``
+    (signed 32-bit distance): every chunk is read by some tile, whose wait then
+    gives up.
+    """
+    A_bits = np.asarray(A_bits)
+    M = A_bits.shape[0]
+    if P < 1 or not (0 <= rank < P) or M % P:
+        raise ValueError("need P >= 1, 0 <= rank < P and P dividing M")
+    S = M // P
+    if S and (chunk_rows <= 0 or S % chunk_rows):
+        raise ValueError("chunk_rows must divide the shard height")
+    C = local_partial(A_bits, B_bits)
+    ready = np.asarray(ready, dtype=np.uint32)
+    error = 0
+    for p in range(P):
+        if p == rank:
+            continue
+        for c in range(ready.shape[1]):
+            d = (int(ready[p, c]) - (expected & 0xFFFFFFFF)) & 0xFFFFFFFF
+            if d >= 1 << 31:
+                error = 1
+    return C, error
 

@@ -541,3 +541,22 @@ def test_push_from_every_rank_gives_the_full_sum():
     with pytest.raises(ValueError):
         orc.push_share(np.zeros((12, 4)), np.zeros((2, 4, 4)), 3, 0, 2)
 
+
+def test_ag_gemm_is_the_gathered_product():
+    """Each rank's row block of C is that rank's A rows times B (block rows of
+    a product), and only other ranks' late chunks count as errors."""
+    rng = np.random.default_rng(8)
+    P, rank, S, K, N, cr = 4, 2, 6, 5, 7, 3
+    blocks = [rng.integers(-2, 3, (S, K)) for _ in range(P)]
+    B = rng.integers(-2, 3, (K, N))
+    A = np.concatenate(blocks)
+    ready = np.full((P, S // cr), 3, np.uint32)
+    C, err = orc.ag_gemm(_bits(A), _bits(B), ready, P, rank, cr, 3)
+    assert err == 0
+    for p in range(P):
+        assert np.array_equal(C[p * S:(p + 1) * S], blocks[p].astype(np.float64) @ B)
+    ready[rank, 0] = 0                    # this rank's own words are never waited on
+    assert orc.ag_gemm(_bits(A), _bits(B), ready, P, rank, cr, 3)[1] == 0
+    ready[0, 1] = 2                       # another rank's chunk one call behind
+    assert orc.ag_gemm(_bits(A), _bits(B), ready, P, rank, cr, 3)[1] == 1
+
