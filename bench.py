@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run 5 device copies of 512 MiB (counter calibration) and exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ag-gemm", action="store_true",
+                   help="skip the all-gather + GEMM measurement (N x N/8 x N, N = 32768)")
     p.add_argument("--no-push", action="store_true",
                    help="skip the atomic push variant beside the staged share")
     p.add_argument("--no-consumer", action="store_true",
@@ -166,6 +168,29 @@ def measure_push(w, args, torch, gen, pk, steps, warmup):
     rmw = 2 * 4 * w.M * w.N
     return {"kernel_ms": round(ms, 5), "accum_rmw_bytes": rmw,
             "accum_rmw_gbps": round(rmw / (ms * 1e-3) / 1e9, 1)}
+
+
+def measure_ag_gemm(torch, gen, pk, steps, warmup, n=32768, P=8, rank=3, chunk_rows=512):
+    """All-gather + GEMM at the pages' tensor-parallel shape (N x N/8 x N with
+    N = 32768: C [N][N/8] = A_gathered [N][N] * B [N][N/8]), every chunk
+    already arrived (ready words preset), so the time is the GEMM plus the
+    per-tile waits; the GEMM-only mode on the same shape is timed beside it."""
+    w = gen.Workload("ag_gemm", P=1, rank=0, M=n, N=n // 8, K=n, chunk_rows=0,
+                     ab_dist="normal_sqrtk", peer_dist="normal", out_dtype="bf16")
+    A, B, _ = gen.make_inputs(w, "cuda", seed=5)
+    C = torch.empty((n, n // 8), dtype=torch.bfloat16, device="cuda")
+    ready = torch.ones((P, (n // P) // chunk_rows), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    call = pk.BoundAgGemm(A, ready, B, C, err, n, n // 8, n, P, rank, chunk_rows, 1)
+    ms, _ = time_steps(lambda i: call(), 1, warmup, steps, torch)
+    assert int(err.item()) == 0
+    g = pk.BoundCall(A, B, None, None, C, None, n, n // 8, n, P, 0, 0, 0, 1, gemm_only=True)
+    g_ms, _ = time_steps(lambda i: g(), 1, warmup, steps, torch)
+    flops = 2.0 * n * (n // 8) * n
+    return {"M": n, "N": n // 8, "K": n, "P": P, "rank": rank, "chunk_rows": chunk_rows,
+            "tile_order": 1, "kernel_ms": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "gemm_only_kernel_ms": round(g_ms, 4)}
 
 
 def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
@@ -396,6 +421,8 @@ def main():
         line["atomic_push"] = pu
     if not args.no_consumer and w.P > 1:
         line["chunk_consumer"] = measure_consumer(w, args, torch, gen, pk)
+    if not args.no_ag_gemm:
+        line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, max(5, args.steps // 5), 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gen)
     print(json.dumps(line), flush=True)
