@@ -84,6 +84,10 @@ def load():
     lib.pk_ag_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32,
                                ctypes.c_uint32, i32, i32, ctypes.POINTER(_Options), vp]
     lib.pk_ag_gemm.restype = i32
+    lib.pk_gemm_rs_intercu.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                       i32, i32, i32, ctypes.c_uint32, i32, i32,
+                                       ctypes.POINTER(_Options), vp]
+    lib.pk_gemm_rs_intercu.restype = i32
     del u32p
     _lib = lib
     return lib
@@ -326,6 +330,58 @@ class BoundAgGemm:
 
     def __call__(self) -> int:
         return _check(self._fn(*self._args))
+
+
+class BoundInterCU:
+    """pk_gemm_rs_intercu with its arguments checked and marshalled once;
+    calling the object launches call `expected` (the value the call raises
+    the ready words to), which the caller advances between launches with
+    next()."""
+
+    def __init__(self, A, B, peer_partials, send_bufs, out, flags, dest, status, M, N, K, P,
+                 rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
+                 spin_limit=1 << 16, config=0, max_workgroups=0, group_n=0, owned_split=0,
+                 signal_batch=0, stream=None):
+        import torch
+        _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+        _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
+                     out_bf16)
+        for name, t in (("dest", dest), ("status", status)):
+            if t is None or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous device tensor")
+        n = _chunks(M, P, chunk_rows)
+        if n > 0:
+            need = 2 * (int(P) - 1) * (int(M) // int(P)) * int(N)
+            if dest.numel() * dest.element_size() < need:
+                raise ValueError("dest is smaller than the send buffers")
+            if status.dtype != torch.int32 or status.numel() < n:
+                raise ValueError("status must be int32 with one word per chunk")
+        self._keep = (A, B, peer_partials, send_bufs, out, flags, dest, status)
+        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch)
+        self._fn = load().pk_gemm_rs_intercu
+        self._head = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out),
+                      _ptr(flags), _ptr(dest), _ptr(status), int(M), int(N), int(K), int(P),
+                      int(rank), int(chunk_rows), int(tile_order), int(out_bf16))
+        self._tail = (int(num_comm_cus), int(spin_limit), ctypes.byref(self._opts),
+                      _stream(stream))
+        self.expected = int(expected)
+
+    def next(self):
+        self.expected += 1
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._head, ctypes.c_uint32(self.expected & 0xFFFFFFFF),
+                               *self._tail))
+
+
+def pk_gemm_rs_intercu(A, B, peer_partials, send_bufs, out, flags, dest, status, M, N, K, P,
+                       rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
+                       spin_limit=1 << 16, stream=None, **opts) -> int:
+    """Fused share plus the move of every send chunk into dest by dedicated
+    communicator workgroups, in one launch (see pk_gemm_rs.h)."""
+    return BoundInterCU(A, B, peer_partials, send_bufs, out, flags, dest, status, M, N, K, P,
+                        rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
+                        spin_limit, stream=stream, **opts)()
 
 
 def pk_rs_consume(flags, send_bufs, dest, M, N, P, chunk_rows, expected, status,

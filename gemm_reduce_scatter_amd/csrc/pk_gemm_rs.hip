@@ -29,6 +29,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "pk_chunk_move.h"
 #include "pk_gemm_rs.h"
 #include "pk_plan.h"
 
@@ -119,6 +120,10 @@ struct KArgs {
   uint32_t wait_expected;
   int spin_limit;
   int32_t* wait_error;
+  // communicator workgroups (inter-CU schedule): the first n_comm of the
+  // grid move finished send chunks instead of computing tiles
+  int n_comm;
+  pkm::MoveArgs mv;
   Grid g;
   long long total_tiles;
 };
@@ -946,8 +951,18 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous run of walk positions.
-  const int G = gridDim.x;
-  int w = blockIdx.x;
+  // Inter-CU schedule (the pages' communication workers): the first n_comm
+  // workgroups, a multiple of 8 so the XCD of a compute workgroup is still
+  // blockIdx & 7, move finished send chunks into the staging buffers while
+  // the rest compute.  All of them are resident at once (the host sizes the
+  // grid to the device), and every wait they make is bounded.
+  if (a.n_comm > 0 && (int)blockIdx.x < a.n_comm) {
+    pkm::move_chunks<CS::THREADS>(a.mv, blockIdx.x, a.n_comm, tid,
+                                  reinterpret_cast<int*>(lds0));
+    return;
+  }
+  const int G = gridDim.x - a.n_comm;
+  int w = blockIdx.x - a.n_comm;
   if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
 
   // Round k covers walk positions kG .. kG+G-1.  Without the split the
@@ -1175,10 +1190,13 @@ template <class CS, class CO, int MODE, int GS>
 static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_LAUNCH;
-  long long grid = (long long)cu_count(dev) * occupancy_of<CS, CO, MODE, GS>(dev);
+  // communicator workgroups come on top of the compute grid and take its
+  // place on the device, so that every workgroup is resident at once
+  long long grid = (long long)cu_count(dev) * occupancy_of<CS, CO, MODE, GS>(dev) - a.n_comm;
+  if (grid < 1) return PK_ERR_CONFIG;
   if (o && o->max_workgroups > 0 && o->max_workgroups < grid) grid = o->max_workgroups;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS>), dim3((unsigned)(grid + a.n_comm)),
                      dim3(CS::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
 }
@@ -1236,7 +1254,7 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
 static int run(const void* A, const void* B, const void* peers, void* send, void* out,
                uint32_t* flags, long long M, long long N, long long K, int P, int rank,
                int chunk_rows, int tile_order, int out_bf16, const pk_options* o, void* stream,
-               bool push = false) {
+               bool push = false, int n_comm = 0, const pkm::MoveArgs* mv = nullptr) {
   const int v = push ? validate_push(A, B, out, flags, M, N, K, P, rank, chunk_rows, tile_order, o)
                      : validate(A, B, peers, send, out, flags, M, N, K, P, rank, chunk_rows,
                                 tile_order, out_bf16, o);
@@ -1281,6 +1299,12 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.wait_expected = 0;
   a.spin_limit = 1;
   a.wait_error = nullptr;
+  a.n_comm = 0;
+  a.mv = pkm::MoveArgs{};
+  if (mv) {
+    a.n_comm = n_comm;
+    a.mv = *mv;
+  }
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (cfg) {
@@ -1383,6 +1407,38 @@ int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags,
                     const pk_options* opts, void* stream) {
   return pk::run(A, B, nullptr, nullptr, accum, flags, M, N, K, P, rank, chunk_rows, tile_order,
                  0, opts, stream, true);
+}
+
+int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials, void* send_bufs,
+                       void* out, uint32_t* flags, void* dest, int32_t* status, int64_t M,
+                       int64_t N, int64_t K, int P, int rank, int chunk_rows, int tile_order,
+                       int out_bf16, uint32_t expected, int num_comm_cus, int spin_limit,
+                       const pk_options* opts, void* stream) {
+  if (P < 2) return PK_ERR_RANK;
+  if (num_comm_cus < 1 || num_comm_cus > 1024 || spin_limit < 1) return PK_ERR_CONFIG;
+  if (opts && opts->gemm_only) return PK_ERR_CONFIG;
+  const int v = pk::validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
+                             chunk_rows, tile_order, out_bf16, opts);
+  if (v != PK_OK) return v;
+  if (M == 0 || N == 0) return PK_OK;
+  if (!pk::aligned16(dest) || status == nullptr || (reinterpret_cast<uintptr_t>(status) & 3u))
+    return PK_ERR_POINTER;
+  const long long S = M / P, C = S / chunk_rows;
+  pkm::MoveArgs mv{};
+  mv.ready = flags;
+  mv.src = static_cast<const pkm::u32x4*>(send_bufs);
+  mv.dst = static_cast<pkm::u32x4*>(dest);
+  mv.status = status;
+  mv.observed = nullptr;
+  mv.units_per_chunk = (long long)chunk_rows * N / 8;
+  mv.units_per_slot = S * N / 8;
+  mv.C = (int)C;
+  mv.items = (int)((P - 1) * C);
+  mv.expected = expected;
+  mv.spin_limit = spin_limit;
+  const int n_comm = (num_comm_cus + 7) / 8 * 8;   // whole XCD rounds
+  return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
+                 tile_order, out_bf16, opts, stream, false, n_comm, &mv);
 }
 
 int pk_ag_gemm(const void* A, const uint32_t* a_ready, const void* B, void* C, int32_t* error,

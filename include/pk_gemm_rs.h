@@ -140,6 +140,26 @@ int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags,
                     int64_t M, int64_t N, int64_t K, int P, int rank,
                     int chunk_rows, int tile_order, const pk_options* opts, void* stream);
 
+/* Inter-CU schedule (the pages' alternative to the fused epilogue: in the
+ * ParallelKittens summary page, compute workers produce tiles while
+ * dedicated communication workers move them, with "num_comm_sms" tuned per
+ * size; Syncopate section 5.2 backends (4)-(5), load/store on a specialized
+ * SM).  One launch does what pk_gemm_rs_local_ex does (same send_bufs, out
+ * and flags, bit for bit) and, on num_comm_cus dedicated workgroups (rounded
+ * up to a multiple of 8, one XCD round), moves every send chunk into `dest`
+ * as soon as its ready word reaches `expected` (the value this call raises
+ * it to: n for the n-th call on a zeroed flags buffer), as pk_rs_consume
+ * does: dest bf16 [P-1][S][N], status int32 [P-1][S/chunk_rows] (0 moved,
+ * 1 gave up after spin_limit polls).  The compute grid shrinks by those
+ * workgroups so that all of them are resident at once.  P >= 2; opts as
+ * for pk_gemm_rs_local_ex except gemm_only. */
+int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials,
+                       void* send_bufs, void* out, uint32_t* flags, void* dest,
+                       int32_t* status, int64_t M, int64_t N, int64_t K, int P, int rank,
+                       int chunk_rows, int tile_order, int out_bf16, uint32_t expected,
+                       int num_comm_cus, int spin_limit, const pk_options* opts,
+                       void* stream);
+
 /* All-gather + GEMM, the step before the reduce-scatter in a tensor-
  * parallel MLP (ParallelKittens summary page, "Data and Tensor Parallelism:
  * AG+GEMM, GEMM+RS, and GEMM+AR": local shape N x N/8 x N; Syncopate's
