@@ -193,6 +193,37 @@ def measure_ag_gemm(torch, gen, pk, steps, warmup, n=32768, P=8, rank=3, chunk_r
             "gemm_only_kernel_ms": round(g_ms, 4)}
 
 
+def measure_intercu(w, args, torch, gen, pk, steps, warmup, counts=(8, 16, 32, 64)):
+    """The inter-CU schedule on the same share: one launch computes the share
+    on CUs - n workgroups while n communicator workgroups move every send
+    chunk into staging buffers; timed back to back for each n (the ready
+    words count calls, so each launch moves the call it makes)."""
+    s = BufferSet(w, 17, w.chunk_rows, torch, gen, pk)
+    n = (w.P - 1) * (w.S // w.chunk_rows)
+    dest = torch.empty_like(s.send)
+    status = torch.zeros(n, dtype=torch.int32, device="cuda")
+    out_bf16 = 1 if w.out_dtype == "bf16" else 0
+    res = {}
+    calls = 0
+    for nc in counts:
+        call = pk.BoundInterCU(s.A, s.B, s.peers, s.send, s.out, s.flags, dest, status, w.M, w.N,
+                               w.K, w.P, w.rank, w.chunk_rows, w.tile_order, out_bf16, calls + 1,
+                               nc)
+
+        def step(i):
+            nonlocal calls
+            call()
+            call.next()
+            calls += 1
+        ms, _ = time_steps(step, 1, warmup, steps, torch)
+        assert int(status.abs().max()) == 0, "a communicator gave up on a chunk"
+        res[str(nc)] = round(ms * 1e3, 2)
+    assert torch.equal(dest.view(torch.int16), s.send.view(torch.int16))
+    best = min(res, key=res.get)
+    return {"us_per_call_by_comm_cus": res, "best_comm_cus": int(best),
+            "copy_gbps_at_best": round(2 * (w.P - 1) * w.S * w.N * 2 / (res[best] * 1e-6) / 1e9, 1)}
+
+
 def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
     """The chunk consumer beside the producer on the same share.
 
@@ -421,6 +452,8 @@ def main():
         line["atomic_push"] = pu
     if not args.no_consumer and w.P > 1:
         line["chunk_consumer"] = measure_consumer(w, args, torch, gen, pk)
+    if not args.no_consumer and w.P > 1:
+        line["inter_cu"] = measure_intercu(w, args, torch, gen, pk, args.steps, args.warmup)
     if not args.no_ag_gemm:
         line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, max(5, args.steps // 5), 3)
     if not args.no_cpu_baseline:
