@@ -42,7 +42,7 @@ MALL_BYTES = 256 << 20
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="comm_dominant")
     p.add_argument("--tile-order", type=int, default=None)
@@ -86,7 +86,7 @@ class BufferSet:
                    (self.A, self.B, self.peers, self.send, self.out))
 
 
-def time_steps(fn, n_sets, warmup, steps, torch):
+def time_steps(fn, n_sets, warmup, steps, torch, sample=None):
     """Run warmup + timed steps; returns (ms per step, wall seconds).
 
     A step is one launch of the kernel, issued through a pre-bound call so the
@@ -104,6 +104,8 @@ def time_steps(fn, n_sets, warmup, steps, torch):
     for i in range(steps):
         fn((warmup + i) % n_sets)
     t_end.record()
+    if sample is not None:
+        sample()           # the host is ahead: the GPU is still running the steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return t_start.elapsed_time(t_end) / steps, wall
@@ -132,7 +134,17 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         launch[i]()
         calls[i] += 1
 
-    ms_step, wall = time_steps(step, n_sets, warmup, steps, torch)
+    clocks = []
+
+    def sample():
+        for _ in range(20):
+            c = sclk_mhz()
+            if c is None:
+                return
+            clocks.append(c)
+            time.sleep(0.0005)
+
+    ms_step, wall = time_steps(step, n_sets, warmup, steps, torch, sample)
     k_ms = ms_step
     # every ready word counts the calls on its set; every counter is back to 0
     for s, n in zip(sets, calls):
@@ -140,7 +152,8 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         assert int(s.flags[:half].min()) == n and int(s.flags[:half].max()) == n
         assert int(s.flags[half:].abs().max()) == 0
     res = dict(ms_per_step=ms_step, kernel_ms=k_ms, wall_s=wall, n_sets=n_sets,
-               chunk_rows=chunk, tile_order=order)
+               chunk_rows=chunk, tile_order=order,
+               sclk_mhz=(sorted(clocks)[len(clocks) // 2] if clocks else None))
     if gemm_only:
         for s in sets:
             s.gemm_out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
@@ -222,6 +235,32 @@ def measure_intercu(w, args, torch, gen, pk, steps, warmup, counts=(8, 16, 32, 6
     best = min(res, key=res.get)
     return {"us_per_call_by_comm_cus": res, "best_comm_cus": int(best),
             "copy_gbps_at_best": round(2 * (w.P - 1) * w.S * w.N * 2 / (res[best] * 1e-6) / 1e9, 1)}
+
+
+def torch_mm_ms(w, torch, gen, steps=5, warmup=2):
+    """torch.mm (hipBLASLt) on the same bf16 GEMM: run only, as a reference."""
+    A, B, _ = gen.make_inputs(gen.Workload(w.name, P=1, rank=0, M=w.M, N=w.N, K=w.K,
+                                           chunk_rows=0, ab_dist=w.ab_dist, peer_dist="normal",
+                                           out_dtype="bf16"), "cuda", seed=3)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    ms, _ = time_steps(lambda i: torch.mm(A, B, out=C), 1, warmup, steps, torch)
+    return round(ms, 4)
+
+
+def sclk_mhz():
+    """Current shader clock of the first GPU from sysfs (the starred level of
+    pp_dpm_sclk), or None where the file is not readable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.strip().endswith("*"):
+                        return int(line.split(":")[1].strip().rstrip("*").strip().lower()
+                                   .replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
@@ -356,8 +395,14 @@ def cpu_baseline(w, gen, budget_s=12.0):
         if el >= budget_s or n >= 50:
             break
     per = el / n
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(w.algorithmic_bytes() / per / 1e9, 3), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(threads), "kind": "oracle", "cpu_model": model,
             "sample": f"{n} full oracle calls of the {w.name} share ({w.M}x{w.N}x{w.K}, P={w.P}), "
                       f"{per:.3f} s each, fp64 numpy/OpenBLAS",
             "tflops_fp64": round(w.flops() / per / 1e12, 4)}
@@ -431,9 +476,10 @@ def main():
             w2 = gen.WORKLOADS[name]
             r2 = measure(w2, args.__class__(**{**vars(args), "chunk_rows": None,
                                                "tile_order": None}), torch, gen, pk,
-                         metrics, max(5, args.steps // 5), 3, rotate=False,
+                         metrics, min(20, max(5, args.steps // 5)), 3, rotate=False,
                          gemm_only=not args.no_gemm_only)
             sec = {"workload": w2.name, "K": w2.K, "M": w2.M, "tile_order": r2["tile_order"],
+                   "sclk_mhz_during": r2["sclk_mhz"],
                    "chunk_rows": r2["chunk_rows"], "kernel_ms": round(r2["kernel_ms"], 4),
                    "tflops": round(w2.flops() / (r2["kernel_ms"] * 1e-3) / 1e12, 2),
                    "roofline": roofline_of(w2, r2["kernel_ms"], metrics)}
@@ -441,8 +487,9 @@ def main():
                 sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
                 sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
             if not args.no_push:
-                pu = measure_push(w2, args, torch, gen, pk, max(5, args.steps // 5), 3)
+                pu = measure_push(w2, args, torch, gen, pk, min(20, max(5, args.steps // 5)), 3)
                 sec["atomic_push_kernel_ms"] = pu["kernel_ms"]
+            sec["torch_mm_ms"] = torch_mm_ms(w2, torch, gen)
             secs.append(sec)
         if secs:
             line["secondary"] = secs[0] if len(secs) == 1 else secs
@@ -455,7 +502,7 @@ def main():
     if not args.no_consumer and w.P > 1:
         line["inter_cu"] = measure_intercu(w, args, torch, gen, pk, args.steps, args.warmup)
     if not args.no_ag_gemm:
-        line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, max(5, args.steps // 5), 3)
+        line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, min(20, max(5, args.steps // 5)), 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gen)
     print(json.dumps(line), flush=True)
