@@ -1022,8 +1022,23 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
         const TileCoord st = send_item(a.g, s);
         // A send tile's batch is released before the owned sub-tile that
         // rides with it, so the wait covers only send stores and the ready
-        // words rise a sub-tile earlier.
-        if (s < n_own) {
+        // words rise a sub-tile earlier.  A quarter of the workgroups take
+        // the pair the other way round (the sub-tile first, its peers read
+        // into registers, then the send tile): their send tiles are written
+        // later than the rest, which spreads the burst of send stores that
+        // otherwise leaves every CU at once (P = 8; with fewer peer slots the
+        // sub-tile's own work is small and the extra code path would spill).
+        if (GS == 7 && s < n_own && (w & 3) == 0) {
+          const TileCoord ot = owned_item(a.g, s);
+          const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+          process<CO, MODE, GS, kPeersPrefetch>(a, ot.shard, ot.t * CS::BM + sm * CO::BM,
+                                                ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
+                                                lds3, tid, wave, lane, nobg, nopv);
+          __syncthreads();   // the staging area is the send tile's first stage
+          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+                                              lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
+          if (++npend >= a.sig_batch || last) flush(k);
+        } else if (s < n_own) {
           const TileCoord ot = owned_item(a.g, s);
           const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
           const int olr = ot.t * CS::BM + sm * CO::BM, oc = ot.u * CS::BN + sn * CO::BN;
