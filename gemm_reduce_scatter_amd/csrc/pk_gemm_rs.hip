@@ -23,6 +23,11 @@
 //  * one persistent workgroup per CU slot walks the tile order; consecutive
 //    walk positions go to the same XCD so tiles that share A/B panels share
 //    that XCD's L2.
+// The same kernel template runs the library's other entry points through its
+// Mode: a plain GEMM (the standalone reference), the pages' atomic push
+// epilogue, and the all-gather + GEMM whose tiles wait for their A chunks;
+// the inter-CU schedule is the fused mode with communicator workgroups at
+// the front of the grid.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
