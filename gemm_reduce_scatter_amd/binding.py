@@ -88,6 +88,12 @@ def load():
                                        i32, i32, i32, ctypes.c_uint32, i32, i32,
                                        ctypes.POINTER(_Options), vp]
     lib.pk_gemm_rs_intercu.restype = i32
+    lib.pk_gemm_rs_intercu_reduce.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                              i64, i32, i32, i32, i32, i32, ctypes.c_uint32,
+                                              i32, i32, ctypes.POINTER(_Options), vp]
+    lib.pk_gemm_rs_intercu_reduce.restype = i32
+    lib.pk_reduce_piece_words.argtypes = [i64, i64, i32]
+    lib.pk_reduce_piece_words.restype = i64
     del u32p
     _lib = lib
     return lib
@@ -382,6 +388,82 @@ def pk_gemm_rs_intercu(A, B, peer_partials, send_bufs, out, flags, dest, status,
     return BoundInterCU(A, B, peer_partials, send_bufs, out, flags, dest, status, M, N, K, P,
                         rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
                         spin_limit, stream=stream, **opts)()
+
+
+def pk_reduce_piece_words(M, N, P) -> int:
+    return _check(load().pk_reduce_piece_words(int(M), int(N), int(P)))
+
+
+class BoundInterCUReduce:
+    """pk_gemm_rs_intercu_reduce with its arguments checked and marshalled
+    once; calling the object launches call `expected` (the value it raises
+    the piece words to, and waits for on peer_ready), which the caller
+    advances between launches with next()."""
+
+    def __init__(self, A, B, peer_partials, send_bufs, out, flags, presum, piece_ready, error,
+                 M, N, K, P, rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
+                 spin_limit=1 << 16, peer_ready=None, config=0, max_workgroups=0, group_n=0,
+                 owned_split=0, signal_batch=0, stream=None):
+        import torch
+        _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+        _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
+                     out_bf16)
+        for name, t in (("presum", presum), ("piece_ready", piece_ready), ("error", error),
+                        ("peer_ready", peer_ready)):
+            if t is None:
+                if name != "peer_ready":
+                    raise ValueError(f"{name} is required")
+                continue
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous device tensor")
+        if presum.dtype != torch.float32:
+            raise ValueError("presum must be float32")
+        for name, t in (("piece_ready", piece_ready), ("error", error), ("peer_ready", peer_ready)):
+            if t is not None and t.dtype not in (torch.int32, torch.uint32):
+                raise ValueError(f"{name} must be a 32-bit integer tensor")
+        M_, N_, P_ = int(M), int(N), int(P)
+        if P_ >= 1 and M_ > 0 and N_ > 0 and M_ % P_ == 0:
+            S = M_ // P_
+            if presum.numel() < S * N_:
+                raise ValueError(f"presum holds {presum.numel()} floats, needs {S * N_}")
+            words = load().pk_reduce_piece_words(M_, N_, P_)
+            if words >= 0 and piece_ready.numel() < words:
+                raise ValueError(f"piece_ready holds {piece_ready.numel()} words, needs {words}")
+            if error.numel() < 1:
+                raise ValueError("error needs one word")
+            n = _chunks(M, P, chunk_rows)
+            if peer_ready is not None and n > 0 and peer_ready.numel() < n:
+                raise ValueError("peer_ready needs one word per incoming chunk")
+        self._keep = (A, B, peer_partials, send_bufs, out, flags, presum, piece_ready, error,
+                      peer_ready)
+        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch)
+        self._fn = load().pk_gemm_rs_intercu_reduce
+        self._head = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(peer_ready), _ptr(send_bufs),
+                      _ptr(out), _ptr(flags), _ptr(presum), _ptr(piece_ready), _ptr(error),
+                      M_, N_, int(K), P_, int(rank), int(chunk_rows), int(tile_order),
+                      int(out_bf16))
+        self._tail = (int(num_comm_cus), int(spin_limit), ctypes.byref(self._opts),
+                      _stream(stream))
+        self.expected = int(expected)
+
+    def next(self):
+        self.expected += 1
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._head, ctypes.c_uint32(self.expected & 0xFFFFFFFF),
+                               *self._tail))
+
+
+def pk_gemm_rs_intercu_reduce(A, B, peer_partials, send_bufs, out, flags, presum, piece_ready,
+                              error, M, N, K, P, rank, chunk_rows, tile_order, out_bf16,
+                              expected, num_comm_cus, spin_limit=1 << 16, peer_ready=None,
+                              stream=None, **opts) -> int:
+    """Fused share whose owned-shard peer sum is done by dedicated reduction
+    workgroups in the same launch (see pk_gemm_rs.h)."""
+    return BoundInterCUReduce(A, B, peer_partials, send_bufs, out, flags, presum, piece_ready,
+                              error, M, N, K, P, rank, chunk_rows, tile_order, out_bf16,
+                              expected, num_comm_cus, spin_limit, peer_ready, stream=stream,
+                              **opts)()
 
 
 def pk_rs_consume(flags, send_bufs, dest, M, N, P, chunk_rows, expected, status,

@@ -129,6 +129,14 @@ struct KArgs {
   // grid move finished send chunks instead of computing tiles
   int n_comm;
   pkm::MoveArgs mv;
+  // reduction role of the communicators: the fp32 peer sum of the owned
+  // shard [S][N], its counting words per 64 x 64 piece ([ceil(S/64)][piece_cols]),
+  // and null or the ready words [P-1][n_chunks] of the incoming peer chunks
+  // (those wait for wait_expected too)
+  float* presum;
+  uint32_t* piece_ready;
+  int piece_cols;
+  const uint32_t* peer_ready;
   Grid g;
   long long total_tiles;
 };
@@ -518,7 +526,10 @@ __device__ __forceinline__ void signal_batch(const KArgs& a, long long fk, long 
 // atomics into the accumulator of the rank that owns its rows; kAgGemm:
 // all-gather + GEMM, a tile of another rank's rows first waits for the
 // ready words of the A chunks it reads.
-enum Mode : int { kFused = 0, kGemmOnly = 1, kPush = 2, kAgGemm = 3 };
+// kFusedReduce: kFused whose owned items add their local partial to the peer
+// sum that the communicator workgroups wrote into presum.
+enum Mode : int { kFused = 0, kGemmOnly = 1, kPush = 2, kAgGemm = 3, kFusedReduce = 4 };
+constexpr bool staged_mode(int m) { return m == kFused || m == kFusedReduce; }
 
 // ---------------------------------------------------------------------------
 // Epilogue of one work item.  Each wave re-lays its accumulators, one 16-row
@@ -552,8 +563,10 @@ struct Seg {
 //  kPeersPrefetch - every slot of every segment read into registers before
 //                   the item's main loop (GS = P-1);
 //  kPeersPresum   - summed in the background while the workgroup multiplied
-//                   a send tile just before this item (PresumStream).
-enum PeerSource : int { kPeersDirect = 0, kPeersPrefetch = 1, kPeersPresum = 2 };
+//                   a send tile just before this item (PresumStream);
+//  kPeersReduced  - summed by the communicator workgroups into presum (fp32),
+//                   read once its pieces' words have risen (reduce_units).
+enum PeerSource : int { kPeersDirect = 0, kPeersPrefetch = 1, kPeersPresum = 2, kPeersReduced = 3 };
 
 __device__ __forceinline__ void add_bf16x8(float (&t)[8], u32x4 v) {
 #pragma unroll
@@ -702,12 +715,12 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
   constexpr int BATCH =
       SRC != kPeersDirect ? PASSES : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
   static_assert(PASSES % BATCH == 0, "batches tile the passes");
-  const bool owned = MODE == kFused && shard == a.rank;
+  const bool owned = staged_mode(MODE) && shard == a.rank;
   const int c8 = lane % LPR;
   const long long col = (long long)col0 + SG::col(wn, lane);
   const bool col_ok = col < a.N;
   const long long slot_stride = (long long)a.S * a.N;
-  const int slot = MODE == kFused && !owned ? slot_of(shard, a.rank) : 0;
+  const int slot = staged_mode(MODE) && !owned ? slot_of(shard, a.rank) : 0;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
@@ -774,6 +787,16 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
             for (int e = 0; e < 8; ++e) {
               if constexpr (SRC == kPeersPresum) t[b][e] = pv.v[sg][e];
               else t[b][e] = 0.0f;
+            }
+            if constexpr (SRC == kPeersReduced) {
+              const float* ps = a.presum + base[b];
+              const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ps));
+              const u32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ps + 4));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                t[b][e] = __uint_as_float(lo[e]);
+                t[b][4 + e] = __uint_as_float(hi[e]);
+              }
             }
             if constexpr (SRC == kPeersPrefetch) {
 #pragma unroll
@@ -894,6 +917,9 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
     __syncthreads();
   }
   bg.finish(a);
+  if constexpr (SRC == kPeersReduced) {
+    if (shard == a.rank) wait_pieces(a, lrow0, col0, C::BM, C::BN, wave, lane);
+  }
 
   using PVT = typename std::conditional<SRC == kPeersPrefetch, PFT, PV>::type;
   const PVT* src;
@@ -940,6 +966,137 @@ __device__ __forceinline__ void wait_rows(const KArgs& a, const TileCoord& tc, i
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+// Reduction role of the inter-CU schedule.  The peer sum of the owned shard
+// is written into presum by the communicator workgroups in pieces of
+// kPiece x kPiece elements; a piece's word rises by one per call once its
+// sums are visible at device scope (the counting convention of the ready
+// words).
+constexpr int kPiece = 64;
+
+// Wave 0 polls `n` words (word q at `at(q)`), lane l taking q = l, l+64, ...,
+// until each reaches wait_expected (a signed 32-bit distance) or spin_limit
+// polls; a word given up ORs `bit` into *wait_error.  Every wave then
+// acquires at device scope.
+template <class At>
+__device__ __forceinline__ void wait_words(const KArgs& a, int n, int bit, int wave, int lane,
+                                           const At& at) {
+  if (wave == 0) {
+    bool ok = true;
+    for (int q = lane; q < n; q += 64) {
+      const uint32_t* w = at(q);
+      int polls = 0;
+      while ((int32_t)(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       a.wait_expected) < 0) {
+        if (++polls >= a.spin_limit) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!ok) __hip_atomic_fetch_or(a.wait_error, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// An owned item of `rows` x `cols` at (lrow0, col0) waits for the words of
+// the pieces it covers before its epilogue reads presum.
+__device__ __forceinline__ void wait_pieces(const KArgs& a, int lrow0, int col0, int rows,
+                                            int cols, int wave, int lane) {
+  const int r1 = lrow0 + rows < a.S ? lrow0 + rows : a.S;
+  const int c1 = col0 + cols < a.N ? col0 + cols : a.N;
+  const int pr0 = lrow0 / kPiece, pc0 = col0 / kPiece;
+  const int npc = (c1 - 1) / kPiece - pc0 + 1;
+  const int n = ((r1 - 1) / kPiece - pr0 + 1) * npc;
+  wait_words(a, n, 1, wave, lane, [&](int q) {
+    return a.piece_ready + (long long)(pr0 + q / npc) * a.piece_cols + pc0 + q % npc;
+  });
+}
+
+// Communicator workgroup r of nc: the owned items of the walk (the same
+// sub-tiles or whole tiles the compute workgroups take, in the owned
+// shard's walk order, which every tile order shares), items r, r+nc, ...
+// For each: wait for the incoming chunks its rows touch (when peer_ready is
+// given; a word given up ORs 2 into *wait_error and the rows are summed as
+// they are), sum its staged peer partials in ascending slot order from +0
+// in fp32 (GS slots' loads in flight per element group), store the sums
+// into presum, release, and raise the words of its pieces.
+template <int GS, int THREADS>
+__device__ __forceinline__ void reduce_units(const KArgs& a, int r, int nc, int tid, int wave,
+                                             int lane) {
+  const Grid& g = a.g;
+  const int R = g.Rm * g.Rn;
+  const int ur = g.BM / g.Rm, uc = g.BN / g.Rn;
+  const long long n_units = (long long)R * g.Tm * g.Tn;
+  const long long slot_stride = (long long)a.S * a.N;
+  constexpr int U = 4;   // element groups (8 columns) per thread in flight
+  for (long long j = r; j < n_units; j += nc) {
+    const long long i = j / R;
+    const int sub = (int)(j - i * R);
+    int t, u;
+    intra_shard(g, i, t, u);
+    const int r0 = t * g.BM + (sub / g.Rn) * ur;
+    const int c0 = u * g.BN + (sub % g.Rn) * uc;
+    const int nr = ur < a.S - r0 ? ur : a.S - r0;
+    const int ncol = uc < a.N - c0 ? uc : a.N - c0;
+    if (a.peer_ready) {
+      const int ch0 = r0 / a.chunk_rows, nch = (r0 + nr - 1) / a.chunk_rows - ch0 + 1;
+      wait_words(a, (a.P - 1) * nch, 2, wave, lane, [&](int q) {
+        return a.peer_ready + (long long)(q / nch) * a.n_chunks + ch0 + q % nch;
+      });
+    }
+    const int gpr = ncol / 8;
+    const int ng = nr * gpr;
+    for (int g0 = tid; g0 < ng; g0 += U * THREADS) {
+      float acc[U][8];
+      long long base[U];
+      bool ok[U];
+#pragma unroll
+      for (int b = 0; b < U; ++b) {
+        const int gi = g0 + b * THREADS;
+        ok[b] = gi < ng;
+        const int rr = ok[b] ? gi / gpr : 0;
+        base[b] = ok[b] ? (long long)(r0 + rr) * a.N + c0 + (gi - rr * gpr) * 8 : 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] = 0.0f;
+      }
+      for (int j0 = 0; j0 < a.P - 1; j0 += GS) {
+        u32x4 q[U][GS];
+#pragma unroll
+        for (int b = 0; b < U; ++b)
+#pragma unroll
+          for (int jj = 0; jj < GS; ++jj)
+            q[b][jj] = load16(a.peers + (j0 + jj) * slot_stride + base[b]);
+#pragma unroll
+        for (int b = 0; b < U; ++b)
+#pragma unroll
+          for (int jj = 0; jj < GS; ++jj) add_bf16x8(acc[b], q[b][jj]);
+      }
+#pragma unroll
+      for (int b = 0; b < U; ++b) {
+        if (!ok[b]) continue;
+        float* dst = a.presum + base[b];
+        store16(dst, u32x4{__float_as_uint(acc[b][0]), __float_as_uint(acc[b][1]),
+                           __float_as_uint(acc[b][2]), __float_as_uint(acc[b][3])});
+        store16(dst + 4, u32x4{__float_as_uint(acc[b][4]), __float_as_uint(acc[b][5]),
+                               __float_as_uint(acc[b][6]), __float_as_uint(acc[b][7])});
+      }
+    }
+    wait_vm0();   // this thread's sums have reached the cache
+    __syncthreads();
+    if (wave == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and memory
+      const int npc = (ncol + kPiece - 1) / kPiece;
+      const int n = (nr + kPiece - 1) / kPiece * npc;
+      for (int q = lane; q < n; q += 64)
+        __hip_atomic_fetch_add(a.piece_ready + (long long)(r0 / kPiece + q / npc) * a.piece_cols +
+                                   c0 / kPiece + q % npc,
+                               1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 template <class CS, class CO, int MODE, int GS>
 __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   using L = LdsPlan<CS, CO>;
@@ -962,8 +1119,11 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   // the rest compute.  All of them are resident at once (the host sizes the
   // grid to the device), and every wait they make is bounded.
   if (a.n_comm > 0 && (int)blockIdx.x < a.n_comm) {
-    pkm::move_chunks<CS::THREADS>(a.mv, blockIdx.x, a.n_comm, tid,
-                                  reinterpret_cast<int*>(lds0));
+    if constexpr (MODE == kFusedReduce)
+      reduce_units<GS, CS::THREADS>(a, blockIdx.x, a.n_comm, tid, wave, lane);
+    else
+      pkm::move_chunks<CS::THREADS>(a.mv, blockIdx.x, a.n_comm, tid,
+                                    reinterpret_cast<int*>(lds0));
     return;
   }
   const int G = gridDim.x - a.n_comm;
@@ -1016,11 +1176,29 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       if constexpr (MODE == kAgGemm) {
         if (tc.shard != a.rank) wait_rows(a, tc, CS::BM, tid);
       }
-      process<CS, MODE, GS, kPeersDirect>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1,
-                                          lds2, lds3, tid, wave, lane, nobg, nopv);
-      if ((MODE == kFused || MODE == kPush) && tc.shard != a.rank) ++npend;
-      if ((MODE == kFused || MODE == kPush) && npend > 0 && (npend >= a.sig_batch || last))
-        flush(k);
+      constexpr int SRC = MODE == kFusedReduce ? kPeersReduced : kPeersDirect;
+      process<CS, MODE, GS, SRC>(a, tc.shard, tc.t * CS::BM, tc.u * CS::BN, lds0, lds1, lds2,
+                                 lds3, tid, wave, lane, nobg, nopv);
+      constexpr bool SIGNALS = staged_mode(MODE) || MODE == kPush;
+      if (SIGNALS && tc.shard != a.rank) ++npend;
+      if (SIGNALS && npend > 0 && (npend >= a.sig_batch || last)) flush(k);
+    } else if constexpr (MODE == kFusedReduce) {
+      // the owned sub-tile's peer sum comes from the communicators
+      if (s < n_send) {
+        const TileCoord st = send_item(a.g, s);
+        process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+                                            lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
+        if (++npend >= a.sig_batch || last) flush(k);
+      }
+      if (s < n_own) {
+        if (s < n_send) __syncthreads();   // the staging area is the sub-tile's first stage
+        const TileCoord ot = owned_item(a.g, s);
+        const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+        process<CO, MODE, GS, kPeersReduced>(a, ot.shard, ot.t * CS::BM + sm * CO::BM,
+                                             ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
+                                             lds3, tid, wave, lane, nobg, nopv);
+        if (npend > 0 && last) flush(k);
+      }
     } else {
       const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
       if (s < n_send) {
@@ -1236,6 +1414,26 @@ static bool use_owned_split(int cfg, int P, long long S, long long N, long long 
   return whole_tiles < 2LL * kAssumedCUs;
 }
 
+// Staged modes: the peer slots summed per batch of loads are 7 for P = 8
+// (and 15, 22, ...), else 3 or 1; the owned split is compiled for
+// configuration 1 with P - 1 in {1, 3, 7}.
+template <class C, int MODE>
+static int launch_staged(KArgs& a, bool split, const pk_options* o, hipStream_t stream) {
+  if constexpr (__is_same(C, Cfg1)) {
+    if (split) {
+      switch (a.P - 1) {
+        case 7: return launch_as<C, CfgOwned, MODE, 7>(a, o, stream);
+        case 3: return launch_as<C, CfgOwned, MODE, 3>(a, o, stream);
+        default: return launch_as<C, CfgOwned, MODE, 1>(a, o, stream);
+      }
+    }
+  }
+  const int np = a.P - 1;
+  if (np > 0 && np % 7 == 0) return launch_as<C, C, MODE, 7>(a, o, stream);
+  if (np > 0 && np % 3 == 0) return launch_as<C, C, MODE, 3>(a, o, stream);
+  return launch_as<C, C, MODE, 1>(a, o, stream);
+}
+
 template <class C>
 static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t stream) {
   const bool gemm_only = mode == kGemmOnly;
@@ -1245,7 +1443,7 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
   a.g.Tn = ceil_div(a.N, C::BN);
   a.g.group_n = (o && o->group_n > 0) ? o->group_n : default_group_n(kCfgs[0], a.g.Tn);
   a.g.Rm = a.g.Rn = 1;
-  const bool split = mode == kFused && use_owned_split(cfg, a.P, a.S, a.N, a.g.total(), o);
+  const bool split = staged_mode(mode) && use_owned_split(cfg, a.P, a.S, a.N, a.g.total(), o);
   if (split) {
     a.g.Rm = C::BM / CfgOwned::BM;
     a.g.Rn = C::BN / CfgOwned::BN;
@@ -1255,26 +1453,25 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
   if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
   if (mode == kPush) return launch_as<C, C, kPush, 1>(a, o, stream);
   if (mode == kAgGemm) return launch_as<C, C, kAgGemm, 1>(a, o, stream);
-  if constexpr (__is_same(C, Cfg1)) {
-    if (split) {
-      switch (a.P - 1) {
-        case 7: return launch_as<C, CfgOwned, kFused, 7>(a, o, stream);
-        case 3: return launch_as<C, CfgOwned, kFused, 3>(a, o, stream);
-        default: return launch_as<C, CfgOwned, kFused, 1>(a, o, stream);
-      }
-    }
-  }
-  // peer slots summed per batch of loads: 7 for P = 8 (and 15, 22, ...)
-  const int np = a.P - 1;
-  if (np > 0 && np % 7 == 0) return launch_as<C, C, kFused, 7>(a, o, stream);
-  if (np > 0 && np % 3 == 0) return launch_as<C, C, kFused, 3>(a, o, stream);
-  return launch_as<C, C, kFused, 1>(a, o, stream);
+  if (mode == kFusedReduce) return launch_staged<C, kFusedReduce>(a, split, o, stream);
+  return launch_staged<C, kFused>(a, split, o, stream);
 }
+
+// Reduction role of the communicators (pk_gemm_rs_intercu_reduce).
+struct RedArgs {
+  float* presum;
+  uint32_t* piece_ready;
+  const uint32_t* peer_ready;
+  int32_t* error;
+  uint32_t expected;
+  int spin_limit;
+};
 
 static int run(const void* A, const void* B, const void* peers, void* send, void* out,
                uint32_t* flags, long long M, long long N, long long K, int P, int rank,
                int chunk_rows, int tile_order, int out_bf16, const pk_options* o, void* stream,
-               bool push = false, int n_comm = 0, const pkm::MoveArgs* mv = nullptr) {
+               bool push = false, int n_comm = 0, const pkm::MoveArgs* mv = nullptr,
+               const RedArgs* red = nullptr) {
   const int v = push ? validate_push(A, B, out, flags, M, N, K, P, rank, chunk_rows, tile_order, o)
                      : validate(A, B, peers, send, out, flags, M, N, K, P, rank, chunk_rows,
                                 tile_order, out_bf16, o);
@@ -1291,7 +1488,7 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.N = (int)N;
   a.K = (int)K;
   const bool gemm_only = !push && o && o->gemm_only;
-  const int mode = push ? kPush : gemm_only ? kGemmOnly : kFused;
+  const int mode = push ? kPush : gemm_only ? kGemmOnly : red ? kFusedReduce : kFused;
   if (gemm_only) {
     // One shard covering every row, nothing sent.
     a.P = 1;
@@ -1321,9 +1518,23 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.wait_error = nullptr;
   a.n_comm = 0;
   a.mv = pkm::MoveArgs{};
+  a.presum = nullptr;
+  a.piece_ready = nullptr;
+  a.piece_cols = 0;
+  a.peer_ready = nullptr;
   if (mv) {
     a.n_comm = n_comm;
     a.mv = *mv;
+  }
+  if (red) {
+    a.n_comm = n_comm;
+    a.presum = red->presum;
+    a.piece_ready = red->piece_ready;
+    a.piece_cols = ceil_div(N, kPiece);
+    a.peer_ready = red->peer_ready;
+    a.wait_expected = red->expected;
+    a.spin_limit = red->spin_limit;
+    a.wait_error = red->error;
   }
   const int cfg = (o && o->config > 0) ? o->config : select_config(M, N, K, a.P);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1459,6 +1670,40 @@ int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials, 
   const int n_comm = (num_comm_cus + 7) / 8 * 8;   // whole XCD rounds
   return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
                  tile_order, out_bf16, opts, stream, false, n_comm, &mv);
+}
+
+int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_partials,
+                              const uint32_t* peer_ready, void* send_bufs, void* out,
+                              uint32_t* flags, float* presum, uint32_t* piece_ready,
+                              int32_t* error, int64_t M, int64_t N, int64_t K, int P, int rank,
+                              int chunk_rows, int tile_order, int out_bf16, uint32_t expected,
+                              int num_comm_cus, int spin_limit, const pk_options* opts,
+                              void* stream) {
+  if (P < 2) return PK_ERR_RANK;
+  if (num_comm_cus < 1 || num_comm_cus > 1024 || spin_limit < 1) return PK_ERR_CONFIG;
+  if (opts && opts->gemm_only) return PK_ERR_CONFIG;
+  const int v = pk::validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
+                             chunk_rows, tile_order, out_bf16, opts);
+  if (v != PK_OK) return v;
+  if (M == 0 || N == 0) return PK_OK;
+  auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (presum == nullptr || !pk::aligned16(presum) || piece_ready == nullptr || !a4(piece_ready) || error == nullptr ||
+      !a4(error) || !a4(peer_ready))
+    return PK_ERR_POINTER;
+  // presum may be the fp32 out itself (each element is read, then written, by
+  // one thread); a bf16 out cannot hold it
+  if (out_bf16 && static_cast<const void*>(presum) == out) return PK_ERR_POINTER;
+  pk::RedArgs red{presum, piece_ready, peer_ready, error, expected, spin_limit};
+  const int n_comm = (num_comm_cus + 7) / 8 * 8;   // whole XCD rounds
+  return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
+                 tile_order, out_bf16, opts, stream, false, n_comm, nullptr, &red);
+}
+
+int64_t pk_reduce_piece_words(int64_t M, int64_t N, int P) {
+  if (P < 1 || P > 64) return PK_ERR_RANK;
+  if (M < 0 || N < 0 || M % P != 0) return PK_ERR_SHAPE;
+  const int64_t S = M / P;
+  return ((S + pk::kPiece - 1) / pk::kPiece) * ((N + pk::kPiece - 1) / pk::kPiece);
 }
 
 int pk_ag_gemm(const void* A, const uint32_t* a_ready, const void* B, void* C, int32_t* error,

@@ -160,6 +160,50 @@ int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials,
                        int num_comm_cus, int spin_limit, const pk_options* opts,
                        void* stream);
 
+/* Inter-CU schedule, reduction role: dedicated workgroups do the owned
+ * shard's reduction while the rest compute (ParallelKittens summary page,
+ * "Scheduling Analysis": inter-SM overlapping gives whole SMs to
+ * communication, with "num_comm_sms" tuned per size as in Figure 5; the
+ * owner-side sum of the staged partials is the reading of the owned-shard
+ * step documented for pk_gemm_rs_local).  One launch leaves send_bufs, out
+ * and flags exactly as pk_gemm_rs_local_ex does, bit for bit, split as:
+ *  - num_comm_cus workgroups (rounded up to a multiple of 8, one XCD round)
+ *    sum the staged peer partials of the owned shard, in ascending slot order
+ *    from +0 in fp32, into `presum` (fp32 [S][N], 16-byte aligned): the
+ *    value the fused epilogue adds the local partial to;
+ *  - the other workgroups run the share; an owned item waits for the
+ *    pieces of presum it covers, then stores out = presum + C_own.
+ * presum may be `out` itself when out is fp32 (each element is read, then
+ * written, by one thread); with a bf16 out it must be a separate buffer.
+ * piece_ready: uint32 [ceil(S/64)][ceil(N/64)] (pk_reduce_piece_words),
+ * 4-byte aligned, zeroed once: the word of the 64 x 64 piece at rows
+ * [64r, 64r+64), columns [64c, 64c+64) of the owned shard rises by one per
+ * call once its sums are visible at device scope; compute workgroups wait
+ * for it to reach `expected` (n for the n-th call on a zeroed buffer; signed
+ * 32-bit distance).  peer_ready: NULL (the peer partials are already staged)
+ * or uint32 [P-1][S/chunk_rows], the ready words of the incoming chunks by
+ * slot: a reduction workgroup first waits for the words of every chunk its
+ * rows touch to reach `expected`, as the owner does in a multi-GPU run.
+ * Every wait polls at most spin_limit >= 1 times; one that gives up ORs 1
+ * (a piece word) or 2 (an incoming chunk word) into *error (int32, device
+ * memory, zeroed by the caller) and the sums are taken from the data as it
+ * is, so a missing producer ends the kernel instead of hanging it.  The
+ * compute grid shrinks by the reduction workgroups so that every workgroup
+ * is resident at once.  P >= 2; opts as for pk_gemm_rs_local_ex except
+ * gemm_only.  Returns PK_OK or PK_ERR_* (arguments checked before any HIP
+ * call). */
+int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_partials,
+                              const uint32_t* peer_ready, void* send_bufs, void* out,
+                              uint32_t* flags, float* presum, uint32_t* piece_ready,
+                              int32_t* error, int64_t M, int64_t N, int64_t K, int P, int rank,
+                              int chunk_rows, int tile_order, int out_bf16, uint32_t expected,
+                              int num_comm_cus, int spin_limit, const pk_options* opts,
+                              void* stream);
+
+/* Number of piece words pk_gemm_rs_intercu_reduce reads and raises:
+ * ceil((M/P)/64) * ceil(N/64), or a negative PK_ERR_* code. */
+int64_t pk_reduce_piece_words(int64_t M, int64_t N, int P);
+
 /* All-gather + GEMM, the step before the reduce-scatter in a tensor-
  * parallel MLP (ParallelKittens summary page, "Data and Tensor Parallelism:
  * AG+GEMM, GEMM+RS, and GEMM+AR": local shape N x N/8 x N; Syncopate's

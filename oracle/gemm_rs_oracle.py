@@ -437,3 +437,55 @@ def ag_gemm(A_bits: np.ndarray, B_bits: np.ndarray, ready: np.ndarray, P: int, r
                 error = 1
     return C, error
 
+
+
+def _behind(word: int, expected: int) -> bool:
+    """True when ``word`` has not reached ``expected`` as a signed 32-bit
+    distance (the reading of the pages' wait taken throughout, so counts may
+    wrap)."""
+    d = (int(word) - (expected & 0xFFFFFFFF)) & 0xFFFFFFFF
+    return d >= 1 << 31
+
+
+def intercu_reduce(peer_bits: np.ndarray, piece_before: np.ndarray, expected: int,
+                   chunk_rows: int, peer_ready=None):
+    """Inter-CU schedule, reduction role: what the reduction workgroups leave
+    beside the share itself (which is the staged share's, reduce_scatter_share).
+
+    [PK] "Scheduling Analysis": with inter-SM overlapping whole SMs do the
+    communication side while the rest compute; here they do the owner-side
+    reduction of the staged peer partials, and the owned-shard value is that
+    peer sum plus the local partial.  [PK] "The Eight PK Primitives": signal
+    adds to a counter and wait spins until it reaches a value.
+
+    ``peer_bits`` (uint16 [P-1, S, N]) are the staged peer partials,
+    ``piece_before`` (uint32 [ceil(S/64), ceil(N/64)]) the piece words before
+    the call (a 64 x 64 piece of the owned shard each, the interface's
+    layout), ``peer_ready`` None or the incoming chunk words (uint32
+    [P-1, S/chunk_rows]).  Returns
+      presum  float64 [S, N]: sum over slots of the peer partials (exact);
+      pieces  uint32: piece_before + 1 (every piece is summed once per call);
+      error   int: bit 2 when an incoming chunk word has not reached
+              ``expected`` (the rows are then summed as they are), bit 1 when
+              a raised piece word is still behind ``expected`` (the owned
+              item covering it then gives up waiting).
+    """
+    peers = bf16_bits_to_f64(np.asarray(peer_bits))
+    n_slots, S, N = peers.shape
+    presum = np.zeros((S, N), dtype=np.float64)
+    for j in range(n_slots):
+        presum = presum + peers[j]
+    piece_before = np.asarray(piece_before, dtype=np.uint32)
+    if piece_before.shape != (-(-S // 64), -(-N // 64)):
+        raise ValueError("one piece word per 64 x 64 block of the shard")
+    pieces = piece_before + np.uint32(1)
+    error = 0
+    if peer_ready is not None:
+        peer_ready = np.asarray(peer_ready, dtype=np.uint32)
+        if chunk_rows <= 0 or S % chunk_rows or peer_ready.shape != (n_slots, S // chunk_rows):
+            raise ValueError("one incoming word per slot and chunk")
+        if any(_behind(w, expected) for w in peer_ready.ravel()):
+            error |= 2
+    if any(_behind(w, expected) for w in pieces.ravel()):
+        error |= 1
+    return presum, pieces, error

@@ -252,3 +252,39 @@ def test_chunk_arrivals_count_overlapping_tiles(M, N, P, chunk, cfg):
         n = sum(1 for t in range(Tm)
                 if max(lo, t * c["BM"]) < min(hi, min((t + 1) * c["BM"], S))) * Tn
         assert pk.pk_chunk_arrivals(M, N, P, chunk, cfg, ci) == n
+
+
+def test_reduce_piece_words():
+    assert pk.pk_reduce_piece_words(4096, 4096, 8) == 8 * 64
+    assert pk.pk_reduce_piece_words(32768, 32768, 8) == 64 * 512
+    assert pk.pk_reduce_piece_words(8 * 130, 72, 8) == 3 * 2        # ragged rows and columns
+    assert pk.pk_reduce_piece_words(0, 64, 2) == 0
+    with pytest.raises(pk.PkError):
+        pk.pk_reduce_piece_words(100, 64, 3)
+    with pytest.raises(pk.PkError):
+        pk.pk_reduce_piece_words(128, 64, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=1, rank=0), -3), (dict(n_comm=0), -5), (dict(n_comm=2000), -5), (dict(spin=0), -5),
+    (dict(presum=0x70004), -1), (dict(presum=None), -1), (dict(piece_ready=None), -1),
+    (dict(piece_ready=0x80002), -1), (dict(error=None), -1), (dict(peer_ready=0x90001), -1),
+    (dict(out_bf16=1, presum=0x50000), -1), (dict(M=255), -2), (dict(tile_order=5), -4),
+])
+def test_intercu_reduce_rejects_before_any_hip_call(kw, code):
+    """Argument errors come back before the entry point touches the device
+    (fake but aligned pointers; a good call would launch)."""
+    import ctypes
+    lib = pk.load()
+    a = dict(A=0x10000, B=0x20000, peers=0x30000, peer_ready=None, send=0x40000, out=0x50000,
+             flags=0x60000, presum=0x70000, piece_ready=0x80000, error=0x90000, M=256, N=256,
+             K=128, P=2, rank=0, chunk_rows=64, tile_order=0, out_bf16=0, expected=1, n_comm=8,
+             spin=16)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    rc = lib.pk_gemm_rs_intercu_reduce(
+        vp(a["A"]), vp(a["B"]), vp(a["peers"]), vp(a["peer_ready"]), vp(a["send"]),
+        vp(a["out"]), vp(a["flags"]), vp(a["presum"]), vp(a["piece_ready"]), vp(a["error"]),
+        a["M"], a["N"], a["K"], a["P"], a["rank"], a["chunk_rows"], a["tile_order"],
+        a["out_bf16"], ctypes.c_uint32(a["expected"]), a["n_comm"], a["spin"], None, None)
+    assert rc == code

@@ -560,3 +560,45 @@ def test_ag_gemm_is_the_gathered_product():
     ready[0, 1] = 2                       # another rank's chunk one call behind
     assert orc.ag_gemm(_bits(A), _bits(B), ready, P, rank, cr, 3)[1] == 1
 
+
+
+def test_intercu_reduce_by_hand():
+    """Two slots of known bf16 values: the workspace holds their sum, every
+    piece word rises by one, and only late words set error bits."""
+    S, N = 130, 72                                   # ragged: 3 x 2 pieces of 64 x 64
+    peers = np.zeros((2, S, N))
+    peers[0] = 1.5
+    peers[1, :, :8] = -0.25
+    peers[1, 128:, 64:] = 40.0
+    presum, pieces, err = orc.intercu_reduce(_bits(peers), np.zeros((3, 2), np.uint32), 1, 65)
+    want = np.full((S, N), 1.5)
+    want[:, :8] = 1.25
+    want[128:, 64:] = 41.5
+    assert np.array_equal(presum, want) and err == 0
+    assert np.array_equal(pieces, np.ones((3, 2), np.uint32))
+    # piece words raised to 4 while the compute side waits for 5: bit 1
+    assert orc.intercu_reduce(_bits(peers), np.full((3, 2), 3, np.uint32), 5, 65)[2] == 1
+    # an incoming chunk one call behind: bit 2; wrap-around counts as arrived
+    ready = np.full((2, 2), 7, np.uint32)
+    assert orc.intercu_reduce(_bits(peers), np.full((3, 2), 6, np.uint32), 7, 65, ready)[2] == 0
+    ready[1, 0] = 6
+    assert orc.intercu_reduce(_bits(peers), np.full((3, 2), 6, np.uint32), 7, 65, ready)[2] == 2
+    wrap = np.full((3, 2), 0xFFFFFFFF, np.uint32)
+    p, w, e = orc.intercu_reduce(_bits(peers), wrap, 0, 65, np.zeros((2, 2), np.uint32))
+    assert np.all(w == 0) and e == 0
+    with pytest.raises(ValueError):
+        orc.intercu_reduce(_bits(peers), np.zeros((2, 2), np.uint32), 1, 65)
+
+
+def test_intercu_reduce_plus_local_partial_is_the_owned_shard():
+    """presum + the rank's own rows of C equals the staged share's out: the
+    reduction role only moves where the peer sum is taken."""
+    rng = np.random.default_rng(9)
+    P, rank, S, K, N = 4, 1, 64, 16, 64
+    A = rng.integers(-2, 3, (P * S, K))
+    B = rng.integers(-2, 3, (K, N))
+    peers = rng.integers(-8, 9, (P - 1, S, N))
+    C = orc.local_partial(_bits(A), _bits(B))
+    share = orc.reduce_scatter_share(C, orc.bf16_bits_to_f64(_bits(peers)), P, rank, 32)
+    presum, _, _ = orc.intercu_reduce(_bits(peers), np.zeros((1, 1), np.uint32), 1, 32)
+    assert np.array_equal(presum + C[rank * S:(rank + 1) * S], share.out)
