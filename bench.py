@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--no-consumer", action="store_true",
                    help="skip the chunk-consumer measurement beside the producer")
     p.add_argument("--no-gemm-only", action="store_true")
+    p.add_argument("--no-reduce", action="store_true",
+                   help="skip the inter-CU reduction role beside the staged share")
     p.add_argument("--sweep", action="store_true",
                    help="large-K schedule sweep: chunk_rows x tile order, one JSON line each")
     return p.parse_args()
@@ -112,7 +114,7 @@ def time_steps(fn, n_sets, warmup, steps, torch, sample=None):
 
 
 def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_only=True,
-            tile_order=None, chunk_rows=None):
+            tile_order=None, chunk_rows=None, reduce_counts=(), reduce_order=None):
     chunk = chunk_rows or args.chunk_rows or w.chunk_rows
     if tile_order is None:
         tile_order = args.tile_order
@@ -163,9 +165,55 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         g_ms, _ = time_steps(lambda i: glaunch[i](), n_sets, warmup, steps, torch)
         res["gemm_only_kernel_ms"] = g_ms
         res["exposed_fraction"] = metrics.exposed_fraction(k_ms, g_ms)
+    if reduce_counts and w.P > 1:
+        res["inter_cu_reduce"] = measure_reduce(w, sets, calls, chunk,
+                                                order if reduce_order is None else reduce_order,
+                                                out_bf16,
+                                                fused_opts, reduce_counts, steps, warmup, k_ms,
+                                                torch, pk)
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def measure_reduce(w, sets, calls, chunk, order, out_bf16, opts, counts, steps, warmup,
+                   fused_ms, torch, pk):
+    """The inter-CU schedule's reduction role on the same buffer sets as the
+    staged share: n workgroups sum the owned shard's peer partials into an
+    fp32 workspace (the fp32 out itself, else a buffer of its own) while the
+    rest compute; timed back to back for each n like the share."""
+    n_sets = len(sets)
+    words = pk.pk_reduce_piece_words(w.M, w.N, w.P)
+    side = []
+    for s in sets:
+        presum = s.out if not out_bf16 else torch.empty((w.S, w.N), dtype=torch.float32,
+                                                         device="cuda")
+        side.append((presum, torch.zeros(words, dtype=torch.int32, device="cuda"),
+                     torch.zeros(1, dtype=torch.int32, device="cuda")))
+    red_calls = [0] * n_sets
+    res = {}
+    for nc in counts:
+        launch = [pk.BoundInterCUReduce(s.A, s.B, s.peers, s.send, s.out, s.flags, ps, pw, er,
+                                        w.M, w.N, w.K, w.P, w.rank, chunk, order, out_bf16,
+                                        red_calls[i] + 1, nc, **opts)
+                  for i, (s, (ps, pw, er)) in enumerate(zip(sets, side))]
+
+        def step(i):
+            launch[i]()
+            launch[i].next()
+            red_calls[i] += 1
+            calls[i] += 1
+        ms, _ = time_steps(step, n_sets, warmup, steps, torch)
+        res[str(nc)] = round(ms * 1e3, 2) if ms < 1 else round(ms, 4)
+    for s, (ps, pw, er), n, nr in zip(sets, side, calls, red_calls):
+        half = s.flags.numel() // 2
+        assert int(s.flags[:half].min()) == n and int(s.flags[half:].abs().max()) == 0
+        assert int(pw.min()) == nr and int(pw.max()) == nr and int(er.item()) == 0
+    best = min(res, key=res.get)
+    unit = "us_per_call_by_comm_cus" if fused_ms < 1 else "ms_per_call_by_comm_cus"
+    scale = 1e3 if fused_ms < 1 else 1.0
+    return {"tile_order": order, unit: res, "best_comm_cus": int(best),
+            "vs_fused": round(res[best] / (fused_ms * scale), 3)}
 
 
 def measure_push(w, args, torch, gen, pk, steps, warmup):
@@ -439,7 +487,8 @@ def main():
         return
 
     r = measure(w, args, torch, gen, pk, metrics, args.steps, args.warmup,
-                gemm_only=not args.no_gemm_only)
+                gemm_only=not args.no_gemm_only,
+                reduce_counts=() if args.no_reduce else (8, 16, 32, 64))
     roof = roofline_of(w, r["kernel_ms"], metrics)
     cfg_id = args.config or pk.pk_select_config(w.M, w.N, w.K, w.P)
     if roof["bound"] == "hbm":
@@ -465,6 +514,8 @@ def main():
     if "gemm_only_kernel_ms" in r:
         line["gemm_only_kernel_ms"] = round(r["gemm_only_kernel_ms"], 5)
         line["exposed_fraction"] = round(r["exposed_fraction"], 4)
+    if "inter_cu_reduce" in r:
+        line["inter_cu_reduce"] = r["inter_cu_reduce"]
     if not args.no_secondary:
         names = ["compute_bound"]
         if args.secondary_all:
@@ -477,7 +528,11 @@ def main():
             r2 = measure(w2, args.__class__(**{**vars(args), "chunk_rows": None,
                                                "tile_order": None}), torch, gen, pk,
                          metrics, min(20, max(5, args.steps // 5)), 3, rotate=False,
-                         gemm_only=not args.no_gemm_only)
+                         gemm_only=not args.no_gemm_only,
+                         reduce_counts=() if args.no_reduce else (16, 32),
+                         # owned tiles wait for the reduction: an order that reaches
+                         # them late (row-major; the owned shard is rank's)
+                         reduce_order=0)
             sec = {"workload": w2.name, "K": w2.K, "M": w2.M, "tile_order": r2["tile_order"],
                    "sclk_mhz_during": r2["sclk_mhz"],
                    "chunk_rows": r2["chunk_rows"], "kernel_ms": round(r2["kernel_ms"], 4),
@@ -486,6 +541,8 @@ def main():
             if "gemm_only_kernel_ms" in r2:
                 sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
                 sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
+            if "inter_cu_reduce" in r2:
+                sec["inter_cu_reduce"] = r2["inter_cu_reduce"]
             if not args.no_push:
                 pu = measure_push(w2, args, torch, gen, pk, min(20, max(5, args.steps // 5)), 3)
                 sec["atomic_push_kernel_ms"] = pu["kernel_ms"]
