@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--no-consumer", action="store_true",
                    help="skip the chunk-consumer measurement beside the producer")
     p.add_argument("--no-gemm-only", action="store_true")
+    p.add_argument("--store-policy", type=int, default=0, choices=(0, 1, 2),
+                   help="output store cache policy: 0 auto, 1 streaming, 2 without the hint")
     p.add_argument("--no-reduce", action="store_true",
                    help="skip the inter-CU reduction role beside the staged share")
     p.add_argument("--sweep", action="store_true",
@@ -125,7 +127,8 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         n_sets = max(2, min(8, math.ceil(1.2 * MALL_BYTES / set_bytes)))
     sets = [BufferSet(w, 17 * i, chunk, torch, gen, pk) for i in range(n_sets)]
     out_bf16 = 1 if w.out_dtype == "bf16" else 0
-    opts = dict(config=args.config, max_workgroups=args.max_workgroups, group_n=args.group_n)
+    opts = dict(config=args.config, max_workgroups=args.max_workgroups, group_n=args.group_n,
+                store_policy=args.store_policy)
     fused_opts = dict(opts, owned_split=args.owned_split)
 
     calls = [0] * n_sets

@@ -30,7 +30,7 @@ class _Options(ctypes.Structure):
     _fields_ = [("config", ctypes.c_int), ("max_workgroups", ctypes.c_int),
                 ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int),
                 ("owned_split", ctypes.c_int), ("signal_batch", ctypes.c_int),
-                ("ready_clock", ctypes.c_void_p)]
+                ("ready_clock", ctypes.c_void_p), ("store_policy", ctypes.c_int)]
 
 
 def lib_path() -> str:
@@ -125,10 +125,10 @@ def _stream(stream):
 
 
 def _opts(config=0, max_workgroups=0, group_n=0, gemm_only=False, owned_split=0,
-          signal_batch=0, ready_clock=None):
+          signal_batch=0, ready_clock=None, store_policy=0):
     return _Options(int(config), int(max_workgroups), int(group_n), 1 if gemm_only else 0,
                     int(owned_split), int(signal_batch),
-                    None if ready_clock is None else ready_clock.data_ptr())
+                    None if ready_clock is None else ready_clock.data_ptr(), int(store_policy))
 
 
 def _check_tensors(A, B, peer_partials, send_bufs, out, flags):
@@ -199,7 +199,7 @@ def pk_gemm_rs_local_bf16out(A, B, peer_partials, send_bufs, out, flags, M, N, K
 def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                         chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0,
                         group_n=0, gemm_only=False, owned_split=0, signal_batch=0,
-                        ready_clock=None, stream=None) -> int:
+                        ready_clock=None, store_policy=0, stream=None) -> int:
     """Fused share with explicit tile configuration / grid / grouping options.
 
     ready_clock: None or a device int64 tensor of (P-1)*S/chunk_rows words that
@@ -208,7 +208,8 @@ def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, 
     _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows, out_bf16,
                  gemm_only)
     _check_clock(ready_clock, M, P, chunk_rows, gemm_only)
-    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch, ready_clock)
+    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch, ready_clock,
+              store_policy)
     return _check(load().pk_gemm_rs_local_ex(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
         int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
@@ -308,11 +309,11 @@ def _ag_args(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows):
 
 def pk_ag_gemm(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows, expected,
                spin_limit=1 << 16, tile_order=1, config=0, max_workgroups=0, group_n=0,
-               stream=None) -> int:
+               store_policy=0, stream=None) -> int:
     """All-gather + GEMM: C = A_gathered * B, each tile of another rank's rows
     waiting for its A chunks' ready words (see pk_gemm_rs.h)."""
     _ag_args(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows)
-    o = _opts(config, max_workgroups, group_n)
+    o = _opts(config, max_workgroups, group_n, store_policy=store_policy)
     return _check(load().pk_ag_gemm(
         _ptr(A), _ptr(a_ready), _ptr(B), _ptr(C), _ptr(error), int(M), int(N), int(K), int(P),
         int(rank), int(chunk_rows), ctypes.c_uint32(int(expected) & 0xFFFFFFFF),
@@ -324,10 +325,10 @@ class BoundAgGemm:
 
     def __init__(self, A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows, expected,
                  spin_limit=1 << 16, tile_order=1, config=0, max_workgroups=0, group_n=0,
-                 stream=None):
+                 store_policy=0, stream=None):
         _ag_args(A, a_ready, B, C, error, M, N, K, P, rank, chunk_rows)
         self._keep = (A, a_ready, B, C, error)
-        self._opts = _opts(config, max_workgroups, group_n)
+        self._opts = _opts(config, max_workgroups, group_n, store_policy=store_policy)
         self._fn = load().pk_ag_gemm
         self._args = (_ptr(A), _ptr(a_ready), _ptr(B), _ptr(C), _ptr(error), int(M), int(N),
                       int(K), int(P), int(rank), int(chunk_rows),
@@ -347,7 +348,7 @@ class BoundInterCU:
     def __init__(self, A, B, peer_partials, send_bufs, out, flags, dest, status, M, N, K, P,
                  rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
                  spin_limit=1 << 16, config=0, max_workgroups=0, group_n=0, owned_split=0,
-                 signal_batch=0, stream=None):
+                 signal_batch=0, store_policy=0, stream=None):
         import torch
         _check_tensors(A, B, peer_partials, send_bufs, out, flags)
         _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
@@ -363,7 +364,8 @@ class BoundInterCU:
             if status.dtype != torch.int32 or status.numel() < n:
                 raise ValueError("status must be int32 with one word per chunk")
         self._keep = (A, B, peer_partials, send_bufs, out, flags, dest, status)
-        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch)
+        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch,
+                           store_policy=store_policy)
         self._fn = load().pk_gemm_rs_intercu
         self._head = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out),
                       _ptr(flags), _ptr(dest), _ptr(status), int(M), int(N), int(K), int(P),
@@ -403,7 +405,7 @@ class BoundInterCUReduce:
     def __init__(self, A, B, peer_partials, send_bufs, out, flags, presum, piece_ready, error,
                  M, N, K, P, rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
                  spin_limit=1 << 16, peer_ready=None, config=0, max_workgroups=0, group_n=0,
-                 owned_split=0, signal_batch=0, stream=None):
+                 owned_split=0, signal_batch=0, store_policy=0, stream=None):
         import torch
         _check_tensors(A, B, peer_partials, send_bufs, out, flags)
         _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
@@ -436,7 +438,8 @@ class BoundInterCUReduce:
                 raise ValueError("peer_ready needs one word per incoming chunk")
         self._keep = (A, B, peer_partials, send_bufs, out, flags, presum, piece_ready, error,
                       peer_ready)
-        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch)
+        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch,
+                           store_policy=store_policy)
         self._fn = load().pk_gemm_rs_intercu_reduce
         self._head = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(peer_ready), _ptr(send_bufs),
                       _ptr(out), _ptr(flags), _ptr(presum), _ptr(piece_ready), _ptr(error),
@@ -508,14 +511,14 @@ class BoundCall:
     def __init__(self, A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                  chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0, group_n=0,
                  gemm_only=False, owned_split=0, signal_batch=0, ready_clock=None,
-                 stream=None):
+                 store_policy=0, stream=None):
         _check_tensors(A, B, peer_partials, send_bufs, out, flags)
         _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
                      out_bf16, gemm_only)
         _check_clock(ready_clock, M, P, chunk_rows, gemm_only)
         self._keep = (A, B, peer_partials, send_bufs, out, flags, ready_clock)
         self._opts = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch,
-                           ready_clock)
+                           ready_clock, store_policy)
         self._fn = load().pk_gemm_rs_local_ex
         self._args = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out),
                       _ptr(flags), int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),
@@ -533,11 +536,12 @@ def pk_flags_words(P, M, chunk_rows) -> int:
 
 def pk_validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
                 tile_order, out_bf16=0, config=0, max_workgroups=0, group_n=0,
-                gemm_only=False, owned_split=0, signal_batch=0) -> int:
+                gemm_only=False, owned_split=0, signal_batch=0, store_policy=0) -> int:
     """Return code the library would give these arguments (no HIP call).
 
     Pointer arguments are plain integers (addresses) or None."""
-    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch)
+    o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch,
+              store_policy=store_policy)
     v = [None if p is None else ctypes.c_void_p(int(p)) for p in
          (A, B, peer_partials, send_bufs, out, flags)]
     return load().pk_validate(*v, int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),

@@ -116,6 +116,7 @@ struct KArgs {
   int N, K;            // N <= 2^24, K <= 2^22 (validated)
   int P, rank, S, chunk_rows, n_chunks;
   int out_bf16;
+  int store_nt;        // output stores carry the non-temporal hint (store16)
   int sig_batch;       // send tiles per ready-word release (>= 1)
   uint64_t* ready_clock;   // null, or [P-1][n_chunks]: device clock when a ready word rose
   // all-gather + GEMM: ready words [P][n_chunks] of the gathered A rows, the
@@ -184,14 +185,21 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// 16-byte store of output data (send chunks, the owned shard, GEMM-only C),
-// written through the L2 to memory (sc0 sc1) as streaming data (nt): nothing
-// here reads it back, and a device-scope release then has few dirty lines to
-// write back.  The compiler does not see the store, so the wait states a
-// following write of its data registers needs are issued here.
-__device__ __forceinline__ void store16(void* p, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(v)
-               : "memory");
+// 16-byte store of output data (send chunks, the owned shard, GEMM-only C,
+// the reduction workspace), written through the L2 to memory (sc0 sc1), so a
+// device-scope release has few dirty lines to write back.  `nt` marks it as
+// streaming data as well: that keeps gigabytes of send chunks from evicting
+// the A and B panels other workgroups reuse, but costs time when the call's
+// streams are small enough to stay in the last-level cache (a runtime choice
+// per call, KArgs::store_nt).  The compiler does not see the store, so the
+// wait states a following write of its data registers needs are issued here.
+__device__ __forceinline__ void store16(void* p, u32x4 v, bool nt) {
+  if (nt)
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" ::"v"(p), "v"(v)
+                 : "memory");
+  else
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(v)
+                 : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -693,13 +701,13 @@ __device__ __forceinline__ void store_out(const KArgs& a, long long base, const 
   if (a.out_bf16) {
     const u32x4 o = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
                      pack_bf16x2(s[6], s[7])};
-    store16(reinterpret_cast<uint16_t*>(a.out) + base, o);
+    store16(reinterpret_cast<uint16_t*>(a.out) + base, o, a.store_nt);
   } else {
     float* dst = reinterpret_cast<float*>(a.out) + base;
     store16(dst, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]),
-                       __float_as_uint(s[3])});
+                       __float_as_uint(s[3])}, a.store_nt);
     store16(dst + 4, u32x4{__float_as_uint(s[4]), __float_as_uint(s[5]), __float_as_uint(s[6]),
-                           __float_as_uint(s[7])});
+                           __float_as_uint(s[7])}, a.store_nt);
   }
 }
 
@@ -768,7 +776,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
               dst = reinterpret_cast<uint16_t*>(a.out) + ((long long)shard * a.S + lr) * a.N + col;
             else
               dst = a.send + (slot * (long long)a.S + lr) * a.N + col;
-            store16(dst, o);
+            store16(dst, o, a.store_nt);
           }
         }
       } else {
@@ -1078,9 +1086,10 @@ __device__ __forceinline__ void reduce_units(const KArgs& a, int r, int nc, int 
         if (!ok[b]) continue;
         float* dst = a.presum + base[b];
         store16(dst, u32x4{__float_as_uint(acc[b][0]), __float_as_uint(acc[b][1]),
-                           __float_as_uint(acc[b][2]), __float_as_uint(acc[b][3])});
+                           __float_as_uint(acc[b][2]), __float_as_uint(acc[b][3])}, a.store_nt);
         store16(dst + 4, u32x4{__float_as_uint(acc[b][4]), __float_as_uint(acc[b][5]),
-                               __float_as_uint(acc[b][6]), __float_as_uint(acc[b][7])});
+                               __float_as_uint(acc[b][6]), __float_as_uint(acc[b][7])},
+                a.store_nt);
       }
     }
     wait_vm0();   // this thread's sums have reached the cache
@@ -1318,6 +1327,7 @@ static int validate(const void* A, const void* B, const void* peers, const void*
   if (o && (o->max_workgroups < 0 || o->group_n < 0)) return PK_ERR_CONFIG;
   if (o && (o->owned_split < -1 || o->owned_split > 1)) return PK_ERR_CONFIG;
   if (o && o->signal_batch < 0) return PK_ERR_CONFIG;
+  if (o && (o->store_policy < 0 || o->store_policy > 2)) return PK_ERR_CONFIG;
   if (o && o->ready_clock && (reinterpret_cast<uintptr_t>(o->ready_clock) & 7u))
     return PK_ERR_POINTER;
   if (M == 0 || N == 0) return PK_OK;     // nothing to write
@@ -1467,6 +1477,17 @@ struct RedArgs {
   int spin_limit;
 };
 
+// Output stores stream past the caches (nt) unless the call's stored bytes
+// fit well inside the 256 MB last-level cache, where the non-temporal hint
+// only slows them (pk_options.store_policy overrides).
+static constexpr long long kStreamStoreBytes = 64LL << 20;
+static int store_nt_for(const pk_options* o, long long stored_bytes) {
+  const int policy = o ? o->store_policy : 0;
+  if (policy == 1) return 1;
+  if (policy == 2) return 0;
+  return stored_bytes > kStreamStoreBytes ? 1 : 0;
+}
+
 static int run(const void* A, const void* B, const void* peers, void* send, void* out,
                uint32_t* flags, long long M, long long N, long long K, int P, int rank,
                int chunk_rows, int tile_order, int out_bf16, const pk_options* o, void* stream,
@@ -1510,6 +1531,9 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.g.S = a.S;
   a.g.N = (int)N;
   a.g.order = tile_order;
+  a.store_nt = store_nt_for(
+      o, gemm_only ? 2LL * M * N
+                   : (long long)a.S * N * (2LL * (a.P - 1) + (out_bf16 ? 2 : 4)));
   a.sig_batch = (o && o->signal_batch > 0) ? o->signal_batch : kDefaultSignalBatch;
   a.ready_clock = o ? o->ready_clock : nullptr;
   a.wait_ready = nullptr;
@@ -1561,7 +1585,8 @@ static int run_ag(const void* A, const uint32_t* a_ready, const void* B, void* C
   if (M > (1LL << 31) || N > kMaxN || K > kMaxK) return PK_ERR_TOO_LARGE;
   if (spin_limit < 1) return PK_ERR_CONFIG;
   if (o && (o->config < 0 || o->config > kNumCfgs || o->max_workgroups < 0 || o->group_n < 0 ||
-            o->gemm_only != 0 || o->owned_split == 1 || o->signal_batch < 0))
+            o->gemm_only != 0 || o->owned_split == 1 || o->signal_batch < 0 ||
+            o->store_policy < 0 || o->store_policy > 2))
     return PK_ERR_CONFIG;
   if (M == 0 || N == 0) return PK_OK;
   if (!aligned16(Cout) || (K > 0 && (!aligned16(A) || !aligned16(B)))) return PK_ERR_POINTER;
@@ -1581,6 +1606,7 @@ static int run_ag(const void* A, const uint32_t* a_ready, const void* B, void* C
   a.chunk_rows = chunk_rows > 0 ? chunk_rows : 1;
   a.n_chunks = chunk_rows > 0 ? (int)(S / chunk_rows) : 0;
   a.out_bf16 = 1;
+  a.store_nt = store_nt_for(o, 2LL * M * N);
   a.sig_batch = 1;
   a.wait_ready = a_ready;
   a.wait_expected = expected;

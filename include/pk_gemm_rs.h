@@ -110,6 +110,11 @@ typedef struct pk_options {
   uint64_t* ready_clock; /* NULL, or uint64 [P-1][S/chunk_rows] (8-byte aligned): for
                            each chunk, the 100 MHz device clock when its ready word
                            rose in this call (timing of the chunk consumer only). */
+  int store_policy;     /* cache policy of the output stores (send chunks, out, the
+                           reduction workspace), all written through to memory:
+                           1 streaming (non-temporal hint), 2 without the hint,
+                           0 = auto (streaming when the call stores more than
+                           64 MiB).  Results never depend on it. */
 } pk_options;
 
 /* The fused share with explicit options; out_bf16 selects bf16 (1) or fp32 (0)

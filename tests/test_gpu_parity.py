@@ -211,10 +211,11 @@ def test_outputs_invariant_across_orders_chunks_and_runs():
     ref = None
     for chunk in (64, 128, 256, 512):
         for order in (0, 1, 2):
-            for grid, split, sig in ((0, 0, 0), (37, 0, 1), (0, -1, 3), (100, 1, 1000)):
+            for grid, split, sig, pol in ((0, 0, 0, 0), (37, 0, 1, 1), (0, -1, 3, 2),
+                                          (100, 1, 1000, 1)):
                 share = H.Share(CD, "f32", chunk_rows=chunk)
                 H.run(share, A, B, peers, tile_order=order, max_workgroups=grid,
-                      owned_split=split, signal_batch=sig)
+                      owned_split=split, signal_batch=sig, store_policy=pol)
                 torch.cuda.synchronize()
                 assert torch.equal(share.flags.cpu(), torch.from_numpy(
                     H.expected_flags(CD, chunk).view(np.int32)))

@@ -64,7 +64,8 @@ def _v(**kw):
                           args["rank"], args["chunk_rows"], args["tile_order"],
                           args.get("out_bf16", 0), args.get("config", 0),
                           args.get("max_workgroups", 0), args.get("group_n", 0),
-                          args.get("gemm_only", False), args.get("owned_split", 0))
+                          args.get("gemm_only", False), args.get("owned_split", 0),
+                          store_policy=args.get("store_policy", 0))
 
 
 def test_validate_accepts_good_arguments():
@@ -76,6 +77,8 @@ def test_validate_accepts_good_arguments():
     assert _v(gemm_only=True, peer_partials=None, send_bufs=None, flags=None) == 0
     for cfg in range(1, pk.pk_config_count() + 1):
         assert _v(config=cfg) == 0
+    for pol in (0, 1, 2):
+        assert _v(store_policy=pol) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -86,6 +89,7 @@ def test_validate_accepts_good_arguments():
     (dict(P=0), -3), (dict(rank=2), -3), (dict(rank=-1), -3), (dict(P=65, M=65 * 64), -3),
     (dict(tile_order=3), -4), (dict(tile_order=-1), -4),
     (dict(config=99), -5), (dict(max_workgroups=-1), -5), (dict(owned_split=2), -5),
+    (dict(store_policy=3), -5), (dict(store_policy=-1), -5),
 ])
 def test_validate_rejects(kw, code):
     assert _v(**kw) == code
