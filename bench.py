@@ -517,6 +517,8 @@ def main():
     if "gemm_only_kernel_ms" in r:
         line["gemm_only_kernel_ms"] = round(r["gemm_only_kernel_ms"], 5)
         line["exposed_fraction"] = round(r["exposed_fraction"], 4)
+        line["torch_mm_ms"] = torch_mm_ms(w, torch, gen, steps=max(5, min(args.steps, 50)))
+    line["sclk_mhz_during"] = r["sclk_mhz"]
     if "inter_cu_reduce" in r:
         line["inter_cu_reduce"] = r["inter_cu_reduce"]
     if not args.no_secondary:
