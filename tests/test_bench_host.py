@@ -1,0 +1,60 @@
+"""Host-side logic of bench.py: the one-GPU contract, the roofline object and
+the measured-traffic lookup (no GPU, no kernel launch)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from gemm_reduce_scatter_amd import inputs as gen  # noqa: E402
+from gemm_reduce_scatter_amd import metrics  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    w = gen.WORKLOADS["comm_dominant"]
+    # 228 FLOP per algorithmic byte, below the 312.5 of 2.5 PF / 8 TB/s
+    assert w.flops() / w.algorithmic_bytes() < metrics.PEAK_BF16_DENSE_FLOPS / metrics.PEAK_HBM_BYTES
+    roof = bench.roofline_of(w, 0.040, metrics)
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert roof["achieved"] == pytest.approx(w.algorithmic_bytes() / 40e-6 / 1e9, rel=1e-3)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-3)
+    for name in ("near_threshold", "compute_bound", "large_k"):
+        w2 = gen.WORKLOADS[name]
+        r2 = bench.roofline_of(w2, 7.0, metrics)
+        assert r2["bound"] == "mfma" and r2["unit"] == "TFLOP/s" and r2["peak"] == 2500.0
+        assert r2["achieved"] == pytest.approx(2 * w2.M * w2.N * w2.K / 7e-3 / 1e12, rel=1e-3)
+
+
+def test_traffic_is_null_for_other_kernel_sources(monkeypatch):
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    with open(path) as f:
+        rec = json.loads(f.read())
+    w = gen.WORKLOADS["comm_dominant"]
+    monkeypatch.setattr(bench, "source_digest", lambda: rec["source_sha256"])
+    e = rec["workloads"]["comm_dominant"]
+    want = round(e["fetch_kib"] * 1024 * rec["copy_fetch_factor"]
+                 + e["write_kib"] * 1024 * rec["copy_write_factor"])
+    assert bench.traffic_for(w) == want
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 64)
+    assert bench.traffic_for(w) is None
+    monkeypatch.setattr(bench, "source_digest", lambda: rec["source_sha256"])
+    assert bench.traffic_for(gen.WORKLOADS["tiny"]) is None     # no counters for that share
+
+
+def test_source_digest_covers_every_kernel_source():
+    d = os.path.join(ROOT, "gemm_reduce_scatter_amd", "csrc")
+    names = sorted(os.listdir(d))
+    assert any(n.endswith(".hip") for n in names)
+    assert len(bench.source_digest()) == 64
