@@ -184,7 +184,8 @@ def measure_reduce(w, sets, calls, chunk, order, out_bf16, opts, counts, steps, 
     """The inter-CU schedule's reduction role on the same buffer sets as the
     staged share: n workgroups sum the owned shard's peer partials into an
     fp32 workspace (the fp32 out itself, else a buffer of its own) while the
-    rest compute; timed back to back for each n like the share."""
+    rest compute; n = 0 sums them in the background of the main loops
+    instead.  Timed back to back for each n like the share."""
     n_sets = len(sets)
     words = pk.pk_reduce_piece_words(w.M, w.N, w.P)
     side = []
@@ -489,9 +490,13 @@ def main():
                       flush=True)
         return
 
+    # 0 reduction workgroups: the reduction runs in the background of the
+    # main loops, which needs P = 8 and a grid that holds every 256 x 256 tile
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bg = w.P == 8 and 8 * math.ceil(w.S / 256) * math.ceil(w.N / 256) <= cus
     r = measure(w, args, torch, gen, pk, metrics, args.steps, args.warmup,
                 gemm_only=not args.no_gemm_only,
-                reduce_counts=() if args.no_reduce else (8, 16, 32, 64))
+                reduce_counts=() if args.no_reduce else ((0,) if bg else ()) + (8, 16, 32, 64))
     roof = roofline_of(w, r["kernel_ms"], metrics)
     cfg_id = args.config or pk.pk_select_config(w.M, w.N, w.K, w.P)
     if roof["bound"] == "hbm":

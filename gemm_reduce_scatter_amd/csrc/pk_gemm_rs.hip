@@ -855,15 +855,18 @@ struct LdsPlan {
   static_assert(B0 + BS + B2 + B3 <= 160 * 1024, "fits the 160 KiB LDS of a CU");
 };
 
-// One work item: a tile of configuration C whose first row is shard-local
-// row `lrow0` of shard `shard` and whose first column is `col0`.  `bg` runs
-// in the background of the main loop; an owned item takes its peer sum from
-// source SRC (`pv` for kPeersPresum).
-template <class C, int MODE, int GS, int SRC, class BG, class PV>
-__device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, int col0,
-                                        unsigned char* b0, unsigned char* b1, unsigned char* b2,
-                                        unsigned char* b3, int tid, int wave, int lane, BG& bg,
-                                        const PV& pv) {
+// Main loop of one work item: a tile of configuration C whose first row is
+// shard-local row `lrow0` of shard `shard` and whose first column is `col0`,
+// multiplied into `acc`.  `bg` runs in the background of the main loop; an
+// owned item that takes its peer sum by prefetch (SRC kPeersPrefetch) reads
+// it into `pf`.  On return every stage load has landed and every wave has
+// passed a barrier, so the ring may be refilled.
+template <class C, int GS, int SRC, class BG, class PFT>
+__device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, int col0,
+                                          unsigned char* b0, unsigned char* b1,
+                                          unsigned char* b2, unsigned char* b3, int wave,
+                                          int lane, BG& bg, PFT& pf,
+                                          f32x16 (&acc)[C::FM][C::FN]) {
   constexpr int S = C::STAGES;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const long long row0 = (long long)shard * a.S + lrow0;
@@ -874,7 +877,6 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   rd.init(wm, wn, lane);
   const int nk = (a.K + C::BK - 1) / C::BK;
 
-  f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -889,8 +891,6 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
     if constexpr (S > 2) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
     if constexpr (S > 3) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
   }
-  using PFT = typename std::conditional<SRC == kPeersPrefetch, PeerPrefetch<C, GS>, NoPeers>::type;
-  PFT pf;
   if (nk > 0) {
     // Loads complete in issue order, so this leaves stages 1 .. S-2 in
     // flight; older stores of the previous item are retired too.
@@ -928,7 +928,21 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   if constexpr (SRC == kPeersReduced) {
     if (shard == a.rank) wait_pieces(a, lrow0, col0, C::BM, C::BN, wave, lane);
   }
+}
 
+// One work item: its main loop (main_part), then its epilogue.  An owned
+// item takes its peer sum from source SRC (`pv` for kPeersPresum).
+template <class C, int MODE, int GS, int SRC, class BG, class PV>
+__device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, int col0,
+                                        unsigned char* b0, unsigned char* b1, unsigned char* b2,
+                                        unsigned char* b3, int tid, int wave, int lane, BG& bg,
+                                        const PV& pv) {
+  (void)tid;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  using PFT = typename std::conditional<SRC == kPeersPrefetch, PeerPrefetch<C, GS>, NoPeers>::type;
+  PFT pf;
+  f32x16 acc[C::FM][C::FN];
+  main_part<C, GS, SRC, BG, PFT>(a, shard, lrow0, col0, b0, b1, b2, b3, wave, lane, bg, pf, acc);
   using PVT = typename std::conditional<SRC == kPeersPrefetch, PFT, PV>::type;
   const PVT* src;
   if constexpr (SRC == kPeersPrefetch) src = &pf;
@@ -1178,6 +1192,97 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
     fk = k + 1;
     npend = 0;
   };
+  if constexpr (MODE == kFusedReduce && SPLIT && GS == 7) {
+    if (a.n_comm == 0) {
+      // Reduction in the background of the main loops (no communicator
+      // workgroups): one whole tile per workgroup, P = 8 and sub-tiles of an
+      // eighth of a tile (the host checks both and that the grid holds every
+      // tile).  Workgroup w < n_send multiplies send tile w; workgroup
+      // n_send + t multiplies owned tile t.  While it multiplies, each sums
+      // the staged peer partials of one owned sub-tile (PresumStream): send
+      // tile w sub-tile w % 7 of owned tile w / 7, owned tile t its own
+      // sub-tile 7.  It stores that sum into presum, releases it, and raises
+      // the sub-tile's piece words; then a send tile is sent and signalled,
+      // and an owned tile waits for the pieces of its eight sub-tiles and
+      // stores out = presum + C.  The sums and their order are the fused
+      // epilogue's, so every output is the staged share's, bit for bit.
+      constexpr int R = 8;
+      const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
+      const long long n_tiles = a.g.tiles_per_shard();
+      if (w >= n_send + n_tiles) return;
+      const bool is_send = w < n_send;
+      const long long oi = is_send ? w / (R - 1) : w - n_send;
+      const int osub = is_send ? (int)(w % (R - 1)) : R - 1;
+      int ot, ou;
+      intra_shard(a.g, oi, ot, ou);
+      const int olr = ot * CS::BM + (osub / a.g.Rn) * CO::BM;
+      const int oc = ou * CS::BN + (osub % a.g.Rn) * CO::BN;
+      int shard = a.rank, lrow0 = ot * CS::BM, col0 = ou * CS::BN;
+      if (is_send) {
+        const TileCoord st = send_item(a.g, w);
+        shard = st.shard;
+        lrow0 = st.t * CS::BM;
+        col0 = st.u * CS::BN;
+      }
+      const int nr = CO::BM < a.S - olr ? CO::BM : a.S - olr;
+      const int ncol = CO::BN < a.N - oc ? CO::BN : a.N - oc;
+      if (a.peer_ready && nr > 0 && ncol > 0) {
+        // the incoming chunks the sub-tile's rows touch must have arrived
+        const int ch0 = olr / a.chunk_rows, nch = (olr + nr - 1) / a.chunk_rows - ch0 + 1;
+        wait_words(a, (a.P - 1) * nch, 2, wave, lane, [&](int q) {
+          return a.peer_ready + (long long)(q / nch) * a.n_chunks + ch0 + q % nch;
+        });
+      }
+      PresumStream<CO, GS, CS::STAGES * CS::KK> ps;
+      ps.init(a, olr, oc, wm, wn, lane);
+      f32x16 acc[CS::FM][CS::FN];
+      main_part<CS, GS, kPeersDirect>(a, shard, lrow0, col0, lds0, lds1, lds2, lds3, wave, lane,
+                                      ps, nopv, acc);
+      using SG = Seg<CO>;
+      const int pc = oc + SG::col(wn, lane);
+#pragma unroll
+      for (int fm = 0; fm < CO::FM; ++fm)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int it = 0; it < SG::PASSES; ++it) {
+            const int pr = olr + SG::row(wm, lane, fm, h, it);
+            const int sg = (fm * 2 + h) * SG::PASSES + it;
+            if (pr < a.S && pc < a.N) {
+              float* dst = a.presum + (long long)pr * a.N + pc;
+              store16(dst, u32x4{__float_as_uint(ps.v[sg][0]), __float_as_uint(ps.v[sg][1]),
+                                 __float_as_uint(ps.v[sg][2]), __float_as_uint(ps.v[sg][3])},
+                      a.store_nt);
+              store16(dst + 4, u32x4{__float_as_uint(ps.v[sg][4]), __float_as_uint(ps.v[sg][5]),
+                                     __float_as_uint(ps.v[sg][6]), __float_as_uint(ps.v[sg][7])},
+                      a.store_nt);
+            }
+          }
+      wait_vm0();   // this thread's sums have reached the cache
+      __syncthreads();
+      if (wave == 0 && nr > 0 && ncol > 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and memory
+        const int npc = (ncol + kPiece - 1) / kPiece;
+        const int n = (nr + kPiece - 1) / kPiece * npc;
+        for (int q = lane; q < n; q += 64)
+          __hip_atomic_fetch_add(a.piece_ready + (long long)(olr / kPiece + q / npc) * a.piece_cols +
+                                     oc / kPiece + q % npc,
+                                 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (is_send) {
+        epilogue<CS, MODE, GS, kPeersDirect, NoPeers>(a, shard, lrow0, col0,
+                                                      reinterpret_cast<float*>(lds0), wave, wm,
+                                                      wn, lane, acc, nopv);
+        flush(0);
+      } else {
+        wait_pieces(a, lrow0, col0, CS::BM, CS::BN, wave, lane);
+        epilogue<CS, MODE, GS, kPeersReduced, NoPeers>(a, shard, lrow0, col0,
+                                                       reinterpret_cast<float*>(lds0), wave, wm,
+                                                       wn, lane, acc, nopv);
+      }
+      return;
+    }
+  }
   for (long long k = 0, s = pos(0); s < a.total_tiles; s = pos(++k)) {
     const bool last = pos(k + 1) >= a.total_tiles;
     if constexpr (!SPLIT) {
@@ -1403,6 +1508,10 @@ static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
   long long grid = (long long)cu_count(dev) * occupancy_of<CS, CO, MODE, GS>(dev) - a.n_comm;
   if (grid < 1) return PK_ERR_CONFIG;
   if (o && o->max_workgroups > 0 && o->max_workgroups < grid) grid = o->max_workgroups;
+  // ... and holds every whole tile on its own resident workgroup (the owned
+  // tiles wait for sums that the send tiles' workgroups produce)
+  if (MODE == kFusedReduce && a.n_comm == 0 && grid < (long long)a.P * a.g.tiles_per_shard())
+    return PK_ERR_CONFIG;
   if (grid > a.total_tiles) grid = a.total_tiles;
   hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS>), dim3((unsigned)(grid + a.n_comm)),
                      dim3(CS::THREADS), 0, stream, a);
@@ -1460,6 +1569,11 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
   }
   a.total_tiles = split ? split_pairs(a.g) : a.g.total();
   if (a.total_tiles == 0) return PK_OK;
+  // The reduction in the background of the main loops (reduction role with
+  // no communicator workgroups) runs configuration 1's owned split at P = 8.
+  if (mode == kFusedReduce && a.n_comm == 0 &&
+      (!split || !__is_same(C, Cfg1) || a.P != 8 || a.g.R() != 8))
+    return PK_ERR_CONFIG;
   if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
   if (mode == kPush) return launch_as<C, C, kPush, 1>(a, o, stream);
   if (mode == kAgGemm) return launch_as<C, C, kAgGemm, 1>(a, o, stream);
@@ -1706,7 +1820,7 @@ int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_par
                               int num_comm_cus, int spin_limit, const pk_options* opts,
                               void* stream) {
   if (P < 2) return PK_ERR_RANK;
-  if (num_comm_cus < 1 || num_comm_cus > 1024 || spin_limit < 1) return PK_ERR_CONFIG;
+  if (num_comm_cus < 0 || num_comm_cus > 1024 || spin_limit < 1) return PK_ERR_CONFIG;
   if (opts && opts->gemm_only) return PK_ERR_CONFIG;
   const int v = pk::validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                              chunk_rows, tile_order, out_bf16, opts);

@@ -194,9 +194,21 @@ int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials,
  * memory, zeroed by the caller) and the sums are taken from the data as it
  * is, so a missing producer ends the kernel instead of hanging it.  The
  * compute grid shrinks by the reduction workgroups so that every workgroup
- * is resident at once.  P >= 2; opts as for pk_gemm_rs_local_ex except
- * gemm_only.  Returns PK_OK or PK_ERR_* (arguments checked before any HIP
- * call). */
+ * is resident at once.
+ * num_comm_cus = 0: no dedicated workgroups; the reduction runs in the
+ * background of the main loops instead (the pages' intra-SM overlap applied
+ * to the owner-side sum).  Every whole tile gets its own workgroup.  While a
+ * send tile or an owned tile is multiplied, its workgroup sums the peer
+ * partials of one 64 x 128 eighth of an owned tile (each owned tile's last
+ * eighth by its own workgroup, the other seven by send tiles' workgroups),
+ * stores the sums into presum and raises their pieces.  It then sends its
+ * tile, or, for an owned tile, waits for the tile's pieces and stores
+ * out = presum + C_own.  Same outputs, piece words and error rules as
+ * above.  It needs P = 8, tile configuration 1 with the owned split (not
+ * turned off by opts), and a grid that holds every tile at once
+ * (8 * ceil(S/256) * ceil(N/256) workgroups); otherwise PK_ERR_CONFIG.
+ * P >= 2; opts as for pk_gemm_rs_local_ex except gemm_only.  Returns PK_OK
+ * or PK_ERR_* (arguments checked before any HIP call). */
 int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_partials,
                               const uint32_t* peer_ready, void* send_bufs, void* out,
                               uint32_t* flags, float* presum, uint32_t* piece_ready,

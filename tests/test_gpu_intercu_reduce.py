@@ -240,7 +240,7 @@ def test_reduce_rejects_bad_arguments():
     A, B, peers = gen.make_inputs(w, DEV, seed=57)
     share = H.Share(w, "f32")
     presum, pieces, err = _side(w)
-    with pytest.raises(pk.PkError):      # no reduction workgroups
+    with pytest.raises(pk.PkError):      # no reduction workgroups, and P = 2 has no background reduction
         pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum,
                                      pieces, err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows, 0, 0,
                                      1, 0)
@@ -252,3 +252,130 @@ def test_reduce_rejects_bad_arguments():
         pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum,
                                      pieces[:0], err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
                                      0, 0, 1, 8)
+
+
+# --- reduction in the background of the main loops (no communicator CUs) ---
+# num_comm_cus = 0: every workgroup multiplies one whole tile; while the send
+# tiles' workgroups (and each owned tile's own) multiply, each sums the peer
+# partials of one owned sub-tile into presum and raises its pieces; the owned
+# tiles then add their local partial.  Outputs are the staged share's, bit
+# for bit.
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+def test_background_reduce_matches_staged(order):
+    w = gen.WORKLOADS["comm_dominant"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=61 + order)
+    ref = H.Share(w, "f32")
+    H.run(ref, A, B, peers, tile_order=order)
+    share = H.Share(w, "f32")
+    presum, pieces, err = _side(w)
+    before = np.zeros((-(-w.S // 64), -(-w.N // 64)), np.uint32)
+    pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum, pieces,
+                                 err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows, order, 0, 1, 0)
+    torch.cuda.synchronize()
+    _same(share, ref)
+    _check_side(w, peers, presum, pieces, err, before, 1, exact=False)
+    assert share.canaries_intact()
+
+
+def test_background_reduce_integer_exact_in_place_repeated():
+    """presum is out itself; integer inputs give the oracle's results exactly
+    on each of three calls, and the piece and ready words count the calls."""
+    w = gen.WORKLOADS["comm_dominant"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=64, integer=True)
+    res = orc.gemm_rs_oracle(gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers), w.P,
+                             w.rank, w.chunk_rows)
+    share = H.Share(w, "f32")
+    _, pieces, err = _side(w)
+    call = pk.BoundInterCUReduce(A, B, peers, share.send, share.out, share.flags, share.out,
+                                 pieces, err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
+                                 w.tile_order, 0, 1, 0)
+    half = share.flags.numel() // 2
+    for n in (1, 2, 3):
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(gen.bf16_bits(share.send), res.send_bits)
+        assert np.array_equal(share.out.cpu().numpy().astype(np.float64), res.out)
+        assert int(share.flags[:half].min()) == n and int(share.flags[:half].max()) == n
+        assert int(share.flags[half:].abs().max()) == 0
+        assert np.all(pieces.cpu().numpy() == n) and int(err.item()) == 0
+        call.next()
+    assert share.canaries_intact()
+
+
+def test_background_reduce_incoming_chunk_waits():
+    """peer_ready given: all words at `expected` pass; one word a call behind
+    is given up after a few polls (error bit 2) and the sub-tiles whose rows
+    it covers are summed from the staged partials as they are (here already
+    complete), so the outputs stay the staged share's.  The piece waits share
+    the short spin limit, so in that call the piece words already stand at
+    `expected` and presum already holds the sums: the owned tiles do not
+    wait, and the outcome does not depend on how long the chunk waits took."""
+    w = gen.WORKLOADS["comm_dominant"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=65)
+    ref = H.Share(w, "f32")
+    H.run(ref, A, B, peers)
+    ready = torch.full((w.P - 1, w.S // w.chunk_rows), 1, dtype=torch.int32, device=DEV)
+    for late in (False, True):
+        if late:
+            ready[3, 1] = 0
+        share = H.Share(w, "f32")
+        presum, pieces, err = _side(w)
+        if late:
+            presum.copy_(_peer_sum_f32(peers))
+            pieces.fill_(1)
+        pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum,
+                                     pieces, err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
+                                     w.tile_order, 0, 1, 0, spin_limit=8 if late else 1 << 16,
+                                     peer_ready=ready)
+        torch.cuda.synchronize()
+        _same(share, ref)
+        assert torch.equal(presum, _peer_sum_f32(peers))
+        assert np.all(pieces.cpu().numpy() == (2 if late else 1))
+        assert int(err.item()) == (2 if late else 0)
+
+
+def test_background_reduce_piece_wait_gives_up():
+    """Owned tiles told to wait for call 5 while the pieces reach 1 give up
+    (error bit 1); presum already holds this call's sums, and the send
+    workgroups write the same bits, so the results are the staged share's."""
+    w = gen.WORKLOADS["comm_dominant"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=66)
+    ref = H.Share(w, "f32")
+    H.run(ref, A, B, peers)
+    presum, pieces, err = _side(w)
+    presum.copy_(_peer_sum_f32(peers))
+    share = H.Share(w, "f32")
+    pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum, pieces,
+                                 err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows, w.tile_order, 0,
+                                 5, 0, spin_limit=4)
+    torch.cuda.synchronize()
+    _same(share, ref)
+    assert np.all(pieces.cpu().numpy() == 1)
+    assert int(err.item()) == 1
+
+
+def test_background_reduce_rejects_what_it_cannot_run():
+    """P other than 8, the owned split turned off, or a grid that cannot hold
+    every tile at once: PK_ERR_CONFIG, nothing launched."""
+    w = gen.WORKLOADS["comm_dominant"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=67)
+    share = H.Share(w, "f32")
+    presum, pieces, err = _side(w)
+    args = (A, B, peers, share.send, share.out, share.flags, presum, pieces, err, w.M, w.N, w.K,
+            w.P, w.rank, w.chunk_rows, w.tile_order, 0, 1, 0)
+    for kw in (dict(owned_split=-1), dict(max_workgroups=128), dict(config=2)):
+        with pytest.raises(pk.PkError) as e:
+            pk.pk_gemm_rs_intercu_reduce(*args, **kw)
+        assert e.value.code == -5
+    w4 = gen.WORKLOADS["comm_dominant"].with_(P=4, rank=1)
+    A4, B4, p4 = gen.make_inputs(w4, DEV, seed=68)
+    s4 = H.Share(w4, "f32")
+    pr4, pc4, er4 = _side(w4)
+    with pytest.raises(pk.PkError) as e:
+        pk.pk_gemm_rs_intercu_reduce(A4, B4, p4, s4.send, s4.out, s4.flags, pr4, pc4, er4, w4.M,
+                                     w4.N, w4.K, w4.P, w4.rank, w4.chunk_rows, 0, 0, 1, 0)
+    assert e.value.code == -5
+    torch.cuda.synchronize()
+    assert int(share.flags.abs().max()) == 0 and int(pieces.abs().max()) == 0

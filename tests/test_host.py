@@ -270,7 +270,8 @@ def test_reduce_piece_words():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(P=1, rank=0), -3), (dict(n_comm=0), -5), (dict(n_comm=2000), -5), (dict(spin=0), -5),
+    (dict(P=1, rank=0), -3), (dict(n_comm=0), -5), (dict(n_comm=-1), -5), (dict(n_comm=2000), -5),
+    (dict(spin=0), -5),
     (dict(presum=0x70004), -1), (dict(presum=None), -1), (dict(piece_ready=None), -1),
     (dict(piece_ready=0x80002), -1), (dict(error=None), -1), (dict(peer_ready=0x90001), -1),
     (dict(out_bf16=1, presum=0x50000), -1), (dict(M=255), -2), (dict(tile_order=5), -4),
