@@ -1283,6 +1283,57 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       return;
     }
   }
+  if constexpr (MODE == kFused && SPLIT && GS == 7) {
+    if (n_send <= G && n_own <= G && n_own > n_send) {
+      // One round with workgroups to spare (G - n_send of them hold no send
+      // tile).  Every fourth send tile's workgroup only sends; its owned
+      // sub-tile goes to the spare workgroups, which take their own sub-tile
+      // and then those, round robin, each with its peers read ahead into
+      // registers.  The other send tiles' workgroups pair their tile with
+      // their own sub-tile as in the walk below.  A paired workgroup is the
+      // longest chain (send tile, then sub-tile); the spare ones otherwise
+      // finish after a third of it, and a quarter of the sub-tiles is what
+      // fills them without making them the longest (fewer relieved
+      // workgroups leave more long chains, more overload the spare ones).
+      const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
+      const long long spare = G - n_send;
+      const long long n_relieved = (n_send + 3) / 4;   // send tiles 0, 4, 8, ...
+      const auto owned_ahead = [&](long long j) {
+        const TileCoord ot = owned_item(a.g, j);
+        const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+        process<CO, MODE, GS, kPeersPrefetch>(a, ot.shard, ot.t * CS::BM + sm * CO::BM,
+                                              ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
+                                              lds3, tid, wave, lane, nobg, nopv);
+      };
+      if (w < n_send) {
+        const TileCoord st = send_item(a.g, w);
+        if ((w & 3) == 0) {
+          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+                                              lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
+          flush(0);
+        } else {
+          const TileCoord ot = owned_item(a.g, w);
+          const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+          const int olr = ot.t * CS::BM + sm * CO::BM, oc = ot.u * CS::BN + sn * CO::BN;
+          PresumStream<CO, GS, CS::STAGES * CS::KK> ps;
+          ps.init(a, olr, oc, wm, wn, lane);
+          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+                                              lds1, lds2, lds3, tid, wave, lane, ps, nopv);
+          flush(0);
+          __syncthreads();   // the staging area is the sub-tile's first stage
+          process<CO, MODE, GS, kPeersPresum>(a, ot.shard, olr, oc, lds0, lds1, lds2, lds3, tid,
+                                              wave, lane, nobg, ps);
+        }
+      } else {
+        if (w < n_own) owned_ahead(w);
+        for (long long i = w - n_send; i < n_relieved; i += spare) {
+          __syncthreads();   // the staging area is the next item's first stage
+          owned_ahead(4 * i);
+        }
+      }
+      return;
+    }
+  }
   for (long long k = 0, s = pos(0); s < a.total_tiles; s = pos(++k)) {
     const bool last = pos(k + 1) >= a.total_tiles;
     if constexpr (!SPLIT) {
