@@ -1120,7 +1120,7 @@ __device__ __forceinline__ void reduce_units(const KArgs& a, int r, int nc, int 
   }
 }
 
-template <class CS, class CO, int MODE, int GS>
+template <class CS, class CO, int MODE, int GS, int ONE = 0>
 __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   using L = LdsPlan<CS, CO>;
   constexpr bool SPLIT = !__is_same(CS, CO);
@@ -1283,10 +1283,11 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       return;
     }
   }
-  if constexpr (MODE == kFused && SPLIT && GS == 7) {
-    if (n_send <= G && n_own <= G && n_own > n_send) {
+  if constexpr (ONE == 1) {
+    static_assert(MODE == kFused && SPLIT && GS == 7, "the one-round schedule");
+    {
       // One round with workgroups to spare (G - n_send of them hold no send
-      // tile).  Every fourth send tile's workgroup only sends; its owned
+      // tile; the host launches this instance only then).  Every fourth send tile's workgroup only sends; its owned
       // sub-tile goes to the spare workgroups, which take their own sub-tile
       // and then those, round robin, each with its peers read ahead into
       // registers.  The other send tiles' workgroups pair their tile with
@@ -1333,7 +1334,7 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       }
       return;
     }
-  }
+  } else {   // the walk, round by round
   for (long long k = 0, s = pos(0); s < a.total_tiles; s = pos(++k)) {
     const bool last = pos(k + 1) >= a.total_tiles;
     if constexpr (!SPLIT) {
@@ -1414,6 +1415,7 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
     }
     __syncthreads();   // the staging area is the next item's first stage
   }
+  }   // the walk
 }
 
 // ---------------------------------------------------------------------------
@@ -1564,6 +1566,15 @@ static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
   if (MODE == kFusedReduce && a.n_comm == 0 && grid < (long long)a.P * a.g.tiles_per_shard())
     return PK_ERR_CONFIG;
   if (grid > a.total_tiles) grid = a.total_tiles;
+  if constexpr (MODE == kFused && !__is_same(CS, CO) && GS == 7) {
+    // the owned split in one round with workgroups to spare: its own schedule
+    const long long n_send = split_sends(a.g), n_own = split_owned(a.g);
+    if (n_send <= grid && n_own <= grid && n_own > n_send) {
+      hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS, 1>),
+                         dim3((unsigned)(grid + a.n_comm)), dim3(CS::THREADS), 0, stream, a);
+      return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
+    }
+  }
   hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS>), dim3((unsigned)(grid + a.n_comm)),
                      dim3(CS::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
