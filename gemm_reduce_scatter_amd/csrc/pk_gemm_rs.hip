@@ -1286,16 +1286,17 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   if constexpr (ONE == 1) {
     static_assert(MODE == kFused && SPLIT && GS == 7, "the one-round schedule");
     {
-      // One round with workgroups to spare (G - n_send of them hold no send
-      // tile; the host launches this instance only then).  Every fourth send tile's workgroup only sends; its owned
-      // sub-tile goes to the spare workgroups, which take their own sub-tile
-      // and then those, round robin, each with its peers read ahead into
-      // registers.  The other send tiles' workgroups pair their tile with
-      // their own sub-tile as in the walk below.  A paired workgroup is the
-      // longest chain (send tile, then sub-tile); the spare ones otherwise
-      // finish after a third of it, and a quarter of the sub-tiles is what
-      // fills them without making them the longest (fewer relieved
-      // workgroups leave more long chains, more overload the spare ones).
+      // The owned split in one round with workgroups to spare: G - n_send of
+      // them hold no send tile (the host launches this instance only then).
+      // Every fourth send tile's workgroup only sends; its owned sub-tile
+      // goes to the spare workgroups, which take their own sub-tile and then
+      // those, round robin, each with its peers read ahead into registers.
+      // The other send tiles' workgroups pair their tile with their own
+      // sub-tile as in the walk below.  A paired workgroup is the longest
+      // chain (send tile, then sub-tile); a spare one otherwise finishes
+      // after a third of it.  A quarter of the sub-tiles fills the spare
+      // workgroups without making them the longest: fewer relieved
+      // workgroups leave more long chains, and more overload the spare ones.
       const int wm = wave / CO::WAVES_N, wn = wave % CO::WAVES_N;
       const long long spare = G - n_send;
       const long long n_relieved = (n_send + 3) / 4;   // send tiles 0, 4, 8, ...
