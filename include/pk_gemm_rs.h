@@ -302,7 +302,11 @@ int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
  * whole tile and 0..R-1 for the R sub-tiles of an owned tile under the owned
  * split (owned_split = 1; only configuration 1), where the walk is a list of
  * pairs, each send tile followed by the owned sub-tile that rides with it.
- * Returns the total number of work items or a negative code.  group_n as in
+ * When the split's pairs fit in one round of the grid at P = 8, the kernel
+ * hands the sub-tiles of every fourth pair (pairs 0, 4, 8, ...) to the
+ * workgroups that hold no send tile, and those pairs' workgroups only send;
+ * the list is the same.  Returns the total number of work items or a
+ * negative code.  group_n as in
  * pk_options (0 = auto for this config). */
 int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,
                      int group_n, int owned_split, int32_t* out4, int64_t cap);
