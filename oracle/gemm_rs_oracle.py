@@ -311,11 +311,14 @@ def error_bound(mag: np.ndarray, n_terms: int, bf16_out: bool, ref: np.ndarray,
     A sum of n_terms products evaluated in a working precision with unit
     roundoff u, in any order, differs from the exact value by at most
     gamma_n * sum|terms| with gamma_n = n*u / (1 - n*u) (Higham, "Accuracy and
-    Stability of Numerical Algorithms", 2nd ed., section 3.1).  u = 2**-23
-    (twice the float32 unit roundoff) also covers hardware accumulators that
-    round toward zero.  The tolerance is the larger of that bound and 2 bf16
-    ulps of the reference; a bf16-stored result adds half a bf16 ulp for its
-    final rounding.
+    Stability of Numerical Algorithms", 2nd ed., section 3.1).  The rounding
+    of a matrix core's internal sums is not published; u = 2**-23 is the unit
+    roundoff of a 24-bit significand under chopping (round toward zero), the
+    weakest rounding that keeps each operation's relative error below one ulp
+    (Higham section 2.1: u = 2**(1-t) for chopping, 2**-t for round to
+    nearest with t = 24), so the bound holds under either.  The tolerance is
+    the larger of that bound and 2 bf16 ulps of the reference; a bf16-stored
+    result adds half a bf16 ulp for its final rounding.
     """
     n = float(n_terms)
     gamma = n * u / (1.0 - n * u)

@@ -349,6 +349,62 @@ def test_error_bound_covers_float32_sequential_accumulation():
     assert np.all(np.abs(acc_b - ref) <= tolb)
 
 
+def test_error_bound_closed_forms():
+    # Where the Higham term and the half-ulp term are exact rationals the
+    # tolerance has a closed form.  n u = 4096 * 2**-23 = 2**-11, so
+    # gamma_4096 = 2**-11 / (1 - 2**-11) = 1/2047 exactly.
+    g = 1.0 / 2047.0
+    one = np.array([1.0])
+    # the Higham term dominates: tolerance = gamma * mag
+    t = orc.error_bound(np.array([1000.0]), 4096, bf16_out=False, ref=one)
+    assert t[0] == pytest.approx(1000.0 * g, rel=1e-15)
+    # the 2-ulp floor dominates: 2 * 2**-7 at |ref| = 1, 2 * 2**-4 at |ref| = 12
+    t = orc.error_bound(np.array([1.0, 1.0]), 4096, bf16_out=False, ref=np.array([1.0, -12.0]))
+    assert t[0] == 2.0 ** -6 and t[1] == 2.0 ** -3
+    # a bf16 result adds half a bf16 ulp at |ref| + gamma * mag:
+    # 1 + 1000/2047 = 1.4885.. lies in [1, 2), ulp 2**-7
+    t = orc.error_bound(np.array([1000.0]), 4096, bf16_out=True, ref=one)
+    assert t[0] == pytest.approx(1000.0 * g + 2.0 ** -8, rel=1e-15)
+    # no terms: no rounding error, only the 2-ulp floor
+    t = orc.error_bound(np.array([5.0]), 0, bf16_out=False, ref=np.array([3.0]))
+    assert t[0] == 2.0 * 2.0 ** -6
+    # n = 2**10 terms: gamma = 2**-13 / (1 - 2**-13) = 1/8191
+    t = orc.error_bound(np.array([8191.0 * 64]), 1024, bf16_out=False, ref=one)
+    assert t[0] == pytest.approx(64.0, rel=1e-15)
+
+
+def test_local_partial_abs_by_hand():
+    # Mixed signs: |A|.|B| differs from |A.B| wherever terms cancel.
+    A = np.array([[1.0, -2.0], [-0.5, 3.0]])
+    B = np.array([[3.0, -1.0], [4.0, 0.25]])
+    T = orc.local_partial_abs(_bits(A), _bits(B))
+    assert np.array_equal(T, np.array([[11.0, 1.5], [13.5, 1.25]]))
+    C = orc.local_partial(_bits(A), _bits(B))
+    assert np.array_equal(C, np.array([[-5.0, -1.5], [10.5, 1.25]]))
+    # invariants: |A.B| <= |A|.|B|, with equality for non-negative operands
+    rng = np.random.default_rng(4)
+    Ar = rng.integers(-3, 4, (6, 5)).astype(float)
+    Br = rng.integers(-3, 4, (5, 7)).astype(float)
+    Tr = orc.local_partial_abs(_bits(Ar), _bits(Br))
+    assert np.all(np.abs(orc.local_partial(_bits(Ar), _bits(Br))) <= Tr)
+    assert np.array_equal(Tr, np.abs(Ar) @ np.abs(Br))
+    assert np.array_equal(orc.local_partial_abs(_bits(np.abs(Ar)), _bits(np.abs(Br))),
+                          orc.local_partial(_bits(np.abs(Ar)), _bits(np.abs(Br))))
+
+
+def test_sampled_magnitudes_are_abs_products_plus_peer_magnitudes():
+    w = gen.WORKLOADS["tiny"].with_(P=4, rank=2, M=32, N=16, K=24, chunk_rows=4)
+    A, B, peers = gen.make_inputs(w, seed=5)
+    Ab, Bb, Pb = gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers)
+    rows = np.arange(w.M).repeat(w.N)
+    cols = np.tile(np.arange(w.N), w.M)
+    _, _, mag = orc.gemm_rs_elements(Ab, Bb, Pb, w.P, w.rank, rows, cols)
+    want = orc.local_partial_abs(Ab, Bb)
+    S = w.S
+    want[w.rank * S:(w.rank + 1) * S] += np.sum(np.abs(orc.bf16_bits_to_f64(Pb)), axis=0)
+    np.testing.assert_allclose(mag.reshape(w.M, w.N), want, rtol=1e-14, atol=0)
+
+
 def test_rel_frobenius():
     assert orc.rel_frobenius(np.array([3.0, 4.0]), np.array([3.0, 4.0])) == 0.0
     assert orc.rel_frobenius(np.array([3.0, 4.0]), np.array([0.0, 5.0])) == pytest.approx(
@@ -414,6 +470,8 @@ def _run_pins():
     test_local_partial_real_values_vs_exact_rational()
     for kind in ("row_lo", "row_hi", "col"):
         test_placement_probes(kind)
+    test_error_bound_closed_forms()
+    test_local_partial_abs_by_hand()
 
 
 def test_pins_pass_on_the_real_oracle():
@@ -422,7 +480,8 @@ def test_pins_pass_on_the_real_oracle():
 
 @pytest.mark.parametrize("mistake", ["slot_ring_relative", "slot_no_skip", "drop_last_peer",
                                      "peer_sign", "transposed_b", "double_rounding",
-                                     "own_rows_shift", "decode_truncates"])
+                                     "own_rows_shift", "decode_truncates", "gamma_too_loose",
+                                     "mag_from_raw_bits"])
 def test_planted_mistakes_are_caught(monkeypatch, mistake):
     if mistake == "slot_ring_relative":
         # another plausible convention (slots ordered from rank+1 around the
@@ -471,6 +530,18 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
     elif mistake == "decode_truncates":
         real = orc.bf16_bits_to_f64
         monkeypatch.setattr(orc, "bf16_bits_to_f64", lambda b: np.trunc(real(b)))
+    elif mistake == "gamma_too_loose":
+        # a unit roundoff 1024 times too large (2**-13): every real-valued
+        # elementwise check would pass almost anything
+        real = orc.error_bound
+        monkeypatch.setattr(orc, "error_bound",
+                            lambda mag, n, bf16_out, ref, u=2.0 ** -23: real(mag, n, bf16_out, ref,
+                                                                            u=u * 1024))
+    elif mistake == "mag_from_raw_bits":
+        # magnitudes taken from the bf16 bit patterns as integers, not decoded
+        def bad(A_bits, B_bits):
+            return np.asarray(A_bits, np.float64) @ np.asarray(B_bits, np.float64)
+        monkeypatch.setattr(orc, "local_partial_abs", bad)
     with pytest.raises((AssertionError, IndexError)):
         _run_pins()
 
