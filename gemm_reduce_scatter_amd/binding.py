@@ -26,6 +26,25 @@ class PkError(RuntimeError):
         self.code = code
 
 
+class IncompleteError(RuntimeError):
+    """A launch that waits on other workgroups gave some wait up (a grid that
+    was not resident at once); ``words`` holds the status or error words."""
+
+    def __init__(self, what: str, words):
+        super().__init__(what)
+        self.words = words
+
+
+def read_words(words, stream=None):
+    """Wait until `stream` (default: torch's current stream) has reached the
+    end of the calls issued so far, then return the int32 status or error
+    words as a numpy array."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    s.synchronize()
+    return words.detach().cpu().numpy().view(np.int32).copy()
+
+
 class _Options(ctypes.Structure):
     _fields_ = [("config", ctypes.c_int), ("max_workgroups", ctypes.c_int),
                 ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int),
@@ -381,6 +400,15 @@ class BoundInterCU:
         return _check(self._fn(*self._head, ctypes.c_uint32(self.expected & 0xFFFFFFFF),
                                *self._tail))
 
+    def check(self, stream=None):
+        """After the launches so far: the per-chunk status words; raises
+        IncompleteError when a chunk was given up (its dest rows are not
+        valid; send_bufs, out and flags always are)."""
+        st = read_words(self._keep[7], stream)
+        if np.any(st != 0):
+            raise IncompleteError(f"{int(np.count_nonzero(st))} chunks were not moved", st)
+        return st
+
 
 def pk_gemm_rs_intercu(A, B, peer_partials, send_bufs, out, flags, dest, status, M, N, K, P,
                        rank, chunk_rows, tile_order, out_bf16, expected, num_comm_cus,
@@ -455,6 +483,22 @@ class BoundInterCUReduce:
     def __call__(self) -> int:
         return _check(self._fn(*self._head, ctypes.c_uint32(self.expected & 0xFFFFFFFF),
                                *self._tail))
+
+    def check(self, stream=None) -> int:
+        """After the launches so far: the error word, or IncompleteError when
+        it says `out` is not valid (pk_gemm_rs.h: bit 2, an incoming chunk
+        given up; any bit when presum is out itself).  Bit 1 alone with a
+        separate presum only reports that owned items summed their peers
+        themselves."""
+        presum, out, error = self._keep[6], self._keep[4], self._keep[8]
+        return _check_reduce_error(read_words(error, stream)[0], presum.data_ptr() == out.data_ptr())
+
+
+def _check_reduce_error(e: int, presum_is_out: bool) -> int:
+    if (e & 2) or (e != 0 and presum_is_out):
+        raise IncompleteError(f"reduction role gave up waits (error word {e}): out is not valid",
+                              np.array([e], np.int32))
+    return int(e)
 
 
 def pk_gemm_rs_intercu_reduce(A, B, peer_partials, send_bufs, out, flags, presum, piece_ready,

@@ -133,10 +133,11 @@ struct KArgs {
   // reduction role of the communicators: the fp32 peer sum of the owned
   // shard [S][N], its counting words per 64 x 64 piece ([ceil(S/64)][piece_cols]),
   // and null or the ready words [P-1][n_chunks] of the incoming peer chunks
-  // (those wait for wait_expected too)
+  // (those wait for wait_expected)
   float* presum;
   uint32_t* piece_ready;
   int piece_cols;
+  uint32_t piece_expected;   // the value a piece word reaches in this call
   const uint32_t* peer_ready;
   Grid g;
   long long total_tiles;
@@ -842,6 +843,91 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
   }
 }
 
+// All-gather + GEMM: before a tile of rank tc.shard's rows reads A, one
+// thread waits (the pages' wait primitive) until the ready word of every A
+// chunk the tile's rows touch has reached wait_expected, a signed 32-bit
+// distance so counts may wrap, polling each at most spin_limit times; every
+// wave then acquires, so the loads of the tile see the chunk data.  A wait
+// that gives up sets *wait_error and the tile is computed from whatever the
+// rows hold, so a missing producer ends the kernel instead of hanging it.
+__device__ __forceinline__ void wait_rows(const KArgs& a, const TileCoord& tc, int BM, int tid) {
+  if (tid == 0) {
+    int c0, c1;
+    chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
+    bool all = true;
+    for (int c = c0; c <= c1; ++c) {
+      const uint32_t* w = a.wait_ready + (long long)tc.shard * a.n_chunks + c;
+      int polls = 0;
+      while ((int32_t)(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       a.wait_expected) < 0) {
+        if (++polls >= a.spin_limit) {
+          all = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!all) __hip_atomic_store(a.wait_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Reduction role of the inter-CU schedule.  The peer sum of the owned shard
+// is written into presum by the communicator workgroups in pieces of
+// kPiece x kPiece elements; a piece's word rises by one per call once its
+// sums are visible at device scope (the counting convention of the ready
+// words).
+constexpr int kPiece = 64;
+
+// Wave 0 polls `n` words (word q at `at(q)`), lane l taking q = l, l+64, ...,
+// until each reaches wait_expected (a signed 32-bit distance) or spin_limit
+// polls; a word given up ORs `bit` into *wait_error.  Every wave then
+// acquires at device scope.
+template <class At>
+__device__ __forceinline__ bool wait_words(const KArgs& a, int n, int bit, uint32_t expected,
+                                           int wave, int lane, const At& at) {
+  __shared__ int all_arrived;
+  if (wave == 0) {
+    bool ok = true;
+    for (int q = lane; q < n; q += 64) {
+      const uint32_t* w = at(q);
+      int polls = 0;
+      while ((int32_t)(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       expected) < 0) {
+        if (++polls >= a.spin_limit) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!ok) __hip_atomic_fetch_or(a.wait_error, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool all = __builtin_amdgcn_ballot_w64(!ok) == 0;
+    if (lane == 0) all_arrived = all ? 1 : 0;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const bool all = all_arrived != 0;
+  __syncthreads();   // every wave has read the verdict before the next wait writes it
+  return all;
+}
+
+// An owned item of `rows` x `cols` at (lrow0, col0) waits for the words of
+// the pieces it covers before its epilogue reads presum; false (the same in
+// every wave) when a word was given up.
+__device__ __forceinline__ bool wait_pieces(const KArgs& a, int lrow0, int col0, int rows,
+                                            int cols, int wave, int lane) {
+  const int r1 = lrow0 + rows < a.S ? lrow0 + rows : a.S;
+  const int c1 = col0 + cols < a.N ? col0 + cols : a.N;
+  const int pr0 = lrow0 / kPiece, pc0 = col0 / kPiece;
+  const int npc = (c1 - 1) / kPiece - pc0 + 1;
+  const int n = ((r1 - 1) / kPiece - pr0 + 1) * npc;
+  return wait_words(a, n, 1, a.piece_expected, wave, lane, [&](int q) {
+    return a.piece_ready + (long long)(pr0 + q / npc) * a.piece_cols + pc0 + q % npc;
+  });
+}
+
 // LDS of the kernel: a ring of up to four stage buffers shared by the tile
 // configurations it runs; buffer 0 also holds the epilogue staging area.
 template <class C1, class C2>
@@ -925,9 +1011,6 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
     __syncthreads();
   }
   bg.finish(a);
-  if constexpr (SRC == kPeersReduced) {
-    if (shard == a.rank) wait_pieces(a, lrow0, col0, C::BM, C::BN, wave, lane);
-  }
 }
 
 // One work item: its main loop (main_part), then its epilogue.  An owned
@@ -947,6 +1030,17 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   const PVT* src;
   if constexpr (SRC == kPeersPrefetch) src = &pf;
   else src = &pv;
+  if constexpr (SRC == kPeersReduced) {
+    // An owned item reads the communicators' sums once their pieces have
+    // risen; if a wait gives up (a reduction workgroup that never ran, on a
+    // device shared with other work), it sums its staged peers itself, so
+    // `out` is right either way and the error word tells the caller.
+    if (shard == a.rank && !wait_pieces(a, lrow0, col0, C::BM, C::BN, wave, lane)) {
+      epilogue<C, MODE, GS, kPeersDirect, PVT>(a, shard, lrow0, col0, reinterpret_cast<float*>(b0),
+                                               wave, wm, wn, lane, acc, *src);
+      return;
+    }
+  }
   epilogue<C, MODE, GS, SRC, PVT>(a, shard, lrow0, col0, reinterpret_cast<float*>(b0), wave, wm,
                                   wn, lane, acc, *src);
 }
@@ -958,84 +1052,6 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
 // background, sends, then multiplies the sub-tile and adds that sum.
 // Positions past the end of one list hold only the other (a lone sub-tile
 // reads its peer partials ahead into registers).
-// All-gather + GEMM: before a tile of rank tc.shard's rows reads A, one
-// thread waits (the pages' wait primitive) until the ready word of every A
-// chunk the tile's rows touch has reached wait_expected, a signed 32-bit
-// distance so counts may wrap, polling each at most spin_limit times; every
-// wave then acquires, so the loads of the tile see the chunk data.  A wait
-// that gives up sets *wait_error and the tile is computed from whatever the
-// rows hold, so a missing producer ends the kernel instead of hanging it.
-__device__ __forceinline__ void wait_rows(const KArgs& a, const TileCoord& tc, int BM, int tid) {
-  if (tid == 0) {
-    int c0, c1;
-    chunks_of_row_tile(tc.t, BM, a.S, a.chunk_rows, c0, c1);
-    bool all = true;
-    for (int c = c0; c <= c1; ++c) {
-      const uint32_t* w = a.wait_ready + (long long)tc.shard * a.n_chunks + c;
-      int polls = 0;
-      while ((int32_t)(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                       a.wait_expected) < 0) {
-        if (++polls >= a.spin_limit) {
-          all = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    if (!all) __hip_atomic_store(a.wait_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// Reduction role of the inter-CU schedule.  The peer sum of the owned shard
-// is written into presum by the communicator workgroups in pieces of
-// kPiece x kPiece elements; a piece's word rises by one per call once its
-// sums are visible at device scope (the counting convention of the ready
-// words).
-constexpr int kPiece = 64;
-
-// Wave 0 polls `n` words (word q at `at(q)`), lane l taking q = l, l+64, ...,
-// until each reaches wait_expected (a signed 32-bit distance) or spin_limit
-// polls; a word given up ORs `bit` into *wait_error.  Every wave then
-// acquires at device scope.
-template <class At>
-__device__ __forceinline__ void wait_words(const KArgs& a, int n, int bit, int wave, int lane,
-                                           const At& at) {
-  if (wave == 0) {
-    bool ok = true;
-    for (int q = lane; q < n; q += 64) {
-      const uint32_t* w = at(q);
-      int polls = 0;
-      while ((int32_t)(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                       a.wait_expected) < 0) {
-        if (++polls >= a.spin_limit) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    if (!ok) __hip_atomic_fetch_or(a.wait_error, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// An owned item of `rows` x `cols` at (lrow0, col0) waits for the words of
-// the pieces it covers before its epilogue reads presum.
-__device__ __forceinline__ void wait_pieces(const KArgs& a, int lrow0, int col0, int rows,
-                                            int cols, int wave, int lane) {
-  const int r1 = lrow0 + rows < a.S ? lrow0 + rows : a.S;
-  const int c1 = col0 + cols < a.N ? col0 + cols : a.N;
-  const int pr0 = lrow0 / kPiece, pc0 = col0 / kPiece;
-  const int npc = (c1 - 1) / kPiece - pc0 + 1;
-  const int n = ((r1 - 1) / kPiece - pr0 + 1) * npc;
-  wait_words(a, n, 1, wave, lane, [&](int q) {
-    return a.piece_ready + (long long)(pr0 + q / npc) * a.piece_cols + pc0 + q % npc;
-  });
-}
-
 // Communicator workgroup r of nc: the owned items of the walk (the same
 // sub-tiles or whole tiles the compute workgroups take, in the owned
 // shard's walk order, which every tile order shares), items r, r+nc, ...
@@ -1064,7 +1080,7 @@ __device__ __forceinline__ void reduce_units(const KArgs& a, int r, int nc, int 
     const int ncol = uc < a.N - c0 ? uc : a.N - c0;
     if (a.peer_ready) {
       const int ch0 = r0 / a.chunk_rows, nch = (r0 + nr - 1) / a.chunk_rows - ch0 + 1;
-      wait_words(a, (a.P - 1) * nch, 2, wave, lane, [&](int q) {
+      wait_words(a, (a.P - 1) * nch, 2, a.wait_expected, wave, lane, [&](int q) {
         return a.peer_ready + (long long)(q / nch) * a.n_chunks + ch0 + q % nch;
       });
     }
@@ -1229,7 +1245,7 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       if (a.peer_ready && nr > 0 && ncol > 0) {
         // the incoming chunks the sub-tile's rows touch must have arrived
         const int ch0 = olr / a.chunk_rows, nch = (olr + nr - 1) / a.chunk_rows - ch0 + 1;
-        wait_words(a, (a.P - 1) * nch, 2, wave, lane, [&](int q) {
+        wait_words(a, (a.P - 1) * nch, 2, a.wait_expected, wave, lane, [&](int q) {
           return a.peer_ready + (long long)(q / nch) * a.n_chunks + ch0 + q % nch;
         });
       }
@@ -1274,11 +1290,16 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
                                                       reinterpret_cast<float*>(lds0), wave, wm,
                                                       wn, lane, acc, nopv);
         flush(0);
-      } else {
-        wait_pieces(a, lrow0, col0, CS::BM, CS::BN, wave, lane);
+      } else if (wait_pieces(a, lrow0, col0, CS::BM, CS::BN, wave, lane)) {
         epilogue<CS, MODE, GS, kPeersReduced, NoPeers>(a, shard, lrow0, col0,
                                                        reinterpret_cast<float*>(lds0), wave, wm,
                                                        wn, lane, acc, nopv);
+      } else {
+        // a sub-tile's sums never rose (its workgroup was not resident):
+        // the owned tile sums its staged peers itself
+        epilogue<CS, MODE, GS, kPeersDirect, NoPeers>(a, shard, lrow0, col0,
+                                                      reinterpret_cast<float*>(lds0), wave, wm,
+                                                      wn, lane, acc, nopv);
       }
       return;
     }
@@ -1650,7 +1671,8 @@ struct RedArgs {
   uint32_t* piece_ready;
   const uint32_t* peer_ready;
   int32_t* error;
-  uint32_t expected;
+  uint32_t expected;         // incoming chunk words
+  uint32_t piece_expected;   // piece words
   int spin_limit;
 };
 
@@ -1722,6 +1744,7 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
   a.presum = nullptr;
   a.piece_ready = nullptr;
   a.piece_cols = 0;
+  a.piece_expected = 0;
   a.peer_ready = nullptr;
   if (mv) {
     a.n_comm = n_comm;
@@ -1734,6 +1757,7 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
     a.piece_cols = ceil_div(N, kPiece);
     a.peer_ready = red->peer_ready;
     a.wait_expected = red->expected;
+    a.piece_expected = red->piece_expected;
     a.spin_limit = red->spin_limit;
     a.wait_error = red->error;
   }
@@ -1804,6 +1828,25 @@ static int run_ag(const void* A, const uint32_t* a_ready, const void* B, void* C
     case 5: return launch<Cfg5>(a, kAgGemm, cfg, o, s);
     default: return PK_ERR_CONFIG;
   }
+}
+
+// Arguments of the reduction role that both of its entry points check (the
+// workspace pointers are checked by the caller).
+static int validate_reduce(const void* A, const void* B, const void* peers, const uint32_t* peer_ready,
+                           const void* send, const void* out, const uint32_t* flags,
+                           const int32_t* error, long long M, long long N, long long K, int P,
+                           int rank, int chunk_rows, int tile_order, int out_bf16, int num_comm_cus,
+                           int spin_limit, const pk_options* o) {
+  if (P < 2) return PK_ERR_RANK;
+  if (num_comm_cus < 0 || num_comm_cus > 1024 || spin_limit < 1) return PK_ERR_CONFIG;
+  if (o && o->gemm_only) return PK_ERR_CONFIG;
+  const int v = validate(A, B, peers, send, out, flags, M, N, K, P, rank, chunk_rows, tile_order,
+                         out_bf16, o);
+  if (v != PK_OK) return v;
+  if (M == 0 || N == 0) return PK_OK;
+  auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (error == nullptr || !a4(error) || !a4(peer_ready)) return PK_ERR_POINTER;
+  return PK_OK;
 }
 
 }  // namespace pk
@@ -1882,21 +1925,20 @@ int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_par
                               int chunk_rows, int tile_order, int out_bf16, uint32_t expected,
                               int num_comm_cus, int spin_limit, const pk_options* opts,
                               void* stream) {
-  if (P < 2) return PK_ERR_RANK;
-  if (num_comm_cus < 0 || num_comm_cus > 1024 || spin_limit < 1) return PK_ERR_CONFIG;
-  if (opts && opts->gemm_only) return PK_ERR_CONFIG;
-  const int v = pk::validate(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
-                             chunk_rows, tile_order, out_bf16, opts);
-  if (v != PK_OK) return v;
-  if (M == 0 || N == 0) return PK_OK;
+  const int v = pk::validate_reduce(A, B, peer_partials, peer_ready, send_bufs, out, flags, error,
+                                    M, N, K, P, rank, chunk_rows, tile_order, out_bf16,
+                                    num_comm_cus, spin_limit, opts);
+  if (v != PK_OK || M == 0 || N == 0) return v;
   auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-  if (presum == nullptr || !pk::aligned16(presum) || piece_ready == nullptr || !a4(piece_ready) || error == nullptr ||
-      !a4(error) || !a4(peer_ready))
+  if (presum == nullptr || !pk::aligned16(presum) || piece_ready == nullptr || !a4(piece_ready))
     return PK_ERR_POINTER;
-  // presum may be the fp32 out itself (each element is read, then written, by
-  // one thread); a bf16 out cannot hold it
-  if (out_bf16 && static_cast<const void*>(presum) == out) return PK_ERR_POINTER;
-  pk::RedArgs red{presum, piece_ready, peer_ready, error, expected, spin_limit};
+  // presum may be the fp32 out itself with communicator workgroups (each
+  // element is read, then written, by one thread); not with a bf16 out, and
+  // not in the background mode, where a late send tile's workgroup would
+  // write its bare peer sum over an owned tile that already stored out
+  if (static_cast<const void*>(presum) == out && (out_bf16 || num_comm_cus == 0))
+    return PK_ERR_POINTER;
+  pk::RedArgs red{presum, piece_ready, peer_ready, error, expected, expected, spin_limit};
   const int n_comm = (num_comm_cus + 7) / 8 * 8;   // whole XCD rounds
   return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
                  tile_order, out_bf16, opts, stream, false, n_comm, nullptr, &red);

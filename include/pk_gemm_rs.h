@@ -157,7 +157,14 @@ int pk_gemm_rs_push(const void* A, const void* B, float* accum, uint32_t* flags,
  * does: dest bf16 [P-1][S][N], status int32 [P-1][S/chunk_rows] (0 moved,
  * 1 gave up after spin_limit polls).  The compute grid shrinks by those
  * workgroups so that all of them are resident at once.  P >= 2; opts as
- * for pk_gemm_rs_local_ex except gemm_only. */
+ * for pk_gemm_rs_local_ex except gemm_only.
+ * Co-residency: the communicators wait for chunks that compute workgroups of
+ * the same launch produce, so the move completes only when the whole grid is
+ * resident together (the grid is sized for an otherwise idle device).  On a
+ * device shared with other work a communicator may give up: send_bufs, out
+ * and flags are still right, but `dest` rows are valid only for chunks whose
+ * status is 0; read the status words after the stream has reached the end
+ * of the call. */
 int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials,
                        void* send_bufs, void* out, uint32_t* flags, void* dest,
                        int32_t* status, int64_t M, int64_t N, int64_t K, int P, int rank,
@@ -178,8 +185,10 @@ int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials,
  *    value the fused epilogue adds the local partial to;
  *  - the other workgroups run the share; an owned item waits for the
  *    pieces of presum it covers, then stores out = presum + C_own.
- * presum may be `out` itself when out is fp32 (each element is read, then
- * written, by one thread); with a bf16 out it must be a separate buffer.
+ * presum may be `out` itself when out is fp32 and num_comm_cus > 0 (each
+ * element is read, then written, by one thread); with a bf16 out or in the
+ * background mode (num_comm_cus = 0) it must be a separate buffer
+ * (PK_ERR_POINTER).
  * piece_ready: uint32 [ceil(S/64)][ceil(N/64)] (pk_reduce_piece_words),
  * 4-byte aligned, zeroed once: the word of the 64 x 64 piece at rows
  * [64r, 64r+64), columns [64c, 64c+64) of the owned shard rises by one per
@@ -189,12 +198,21 @@ int pk_gemm_rs_intercu(const void* A, const void* B, const void* peer_partials,
  * or uint32 [P-1][S/chunk_rows], the ready words of the incoming chunks by
  * slot: a reduction workgroup first waits for the words of every chunk its
  * rows touch to reach `expected`, as the owner does in a multi-GPU run.
- * Every wait polls at most spin_limit >= 1 times; one that gives up ORs 1
- * (a piece word) or 2 (an incoming chunk word) into *error (int32, device
- * memory, zeroed by the caller) and the sums are taken from the data as it
- * is, so a missing producer ends the kernel instead of hanging it.  The
- * compute grid shrinks by the reduction workgroups so that every workgroup
- * is resident at once.
+ * Every wait polls at most spin_limit >= 1 times, so a missing producer
+ * ends the kernel instead of hanging it.  A wait that gives up ORs a bit into
+ * *error (int32, device memory, zeroed by the caller): 2 for an incoming chunk
+ * word (the rows are summed as they are), 1 for a piece word (the owned item
+ * then sums its staged peer partials itself, in the same order, so `out` is
+ * unchanged).  The compute grid shrinks by the reduction workgroups so that
+ * every workgroup is resident at once.
+ * Co-residency: piece words are raised by other workgroups of the same
+ * launch, so the split of work pays off only when the whole grid is resident
+ * together (the grid is sized for an otherwise idle device).  Results are
+ * valid when *error reads 0 after the stream has reached the end of the call;
+ * with error bit 1 alone and presum a separate buffer they are valid too.
+ * With presum == out a reduction workgroup that ran late may have stored its
+ * bare peer sum over the owned shard, so then any nonzero error word means
+ * `out` must not be used.
  * num_comm_cus = 0: no dedicated workgroups; the reduction runs in the
  * background of the main loops instead (the pages' intra-SM overlap applied
  * to the owner-side sum).  Every whole tile gets its own workgroup.  While a

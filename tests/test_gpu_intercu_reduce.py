@@ -176,11 +176,17 @@ def test_reduce_waits_for_incoming_chunks():
             pieces.fill_(3)
         else:
             pieces.fill_(2)
-        pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum,
+        call = pk.BoundInterCUReduce(A, B, peers, share.send, share.out, share.flags, presum,
                                      pieces, err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
                                      w.tile_order, 0, 3, 32, spin_limit=8 if late else 1 << 16,
                                      peer_ready=ready)
-        torch.cuda.synchronize()
+        call()
+        if late:
+            # an incoming chunk given up: the binding's check refuses the results
+            with pytest.raises(pk.IncompleteError):
+                call.check()
+        else:
+            assert call.check() == 0
         _same(share, ref)
         _check_side(w, peers, presum, pieces, err, before + (3 if late else 2), 3, exact=False,
                     peer_ready=ready)
@@ -217,19 +223,20 @@ def test_reduce_with_chunks_arriving_during_the_launch():
 
 def test_reduce_piece_wait_gives_up():
     """Compute workgroups told to wait for call 5 while the pieces reach 1
-    give up (error bit 1); the workspace already holds this call's sums, so
-    the results are still the staged share's."""
+    give up (error bit 1) and sum their staged peers themselves: with presum
+    NaN-filled when the launch starts, the results are still the staged
+    share's, bit for bit, and the binding's check accepts them."""
     w = gen.WORKLOADS["comm_dominant"]
     A, B, peers = gen.make_inputs(w, DEV, seed=56)
     ref = H.Share(w, "f32")
     H.run(ref, A, B, peers)
     presum, pieces, err = _side(w)
-    presum.copy_(_peer_sum_f32(peers))
     share = H.Share(w, "f32")
-    pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum, pieces,
+    call = pk.BoundInterCUReduce(A, B, peers, share.send, share.out, share.flags, presum, pieces,
                                  err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows, w.tile_order, 0,
                                  5, 32, spin_limit=4)
-    torch.cuda.synchronize()
+    call()
+    assert call.check() == 1
     _same(share, ref)
     before = np.zeros((-(-w.S // 64), -(-w.N // 64)), np.uint32)
     _check_side(w, peers, presum, pieces, err, before, 5, exact=False)
@@ -252,6 +259,14 @@ def test_reduce_rejects_bad_arguments():
         pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum,
                                      pieces[:0], err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
                                      0, 0, 1, 8)
+    # a bf16 out cannot hold the fp32 sums: presum starting at out's address
+    # (a float buffer whose first half is the bf16 out) is refused by the library
+    both = torch.zeros((w.S, w.N), dtype=torch.float32, device=DEV)
+    out16 = both.view(torch.bfloat16).view(-1)[:w.S * w.N].view(w.S, w.N)
+    with pytest.raises(pk.PkError) as e:
+        pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, out16, share.flags, both, pieces,
+                                     err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows, 0, 1, 1, 8)
+    assert e.value.code == -1
 
 
 # --- reduction in the background of the main loops (no communicator CUs) ---
@@ -279,22 +294,22 @@ def test_background_reduce_matches_staged(order):
     assert share.canaries_intact()
 
 
-def test_background_reduce_integer_exact_in_place_repeated():
-    """presum is out itself; integer inputs give the oracle's results exactly
-    on each of three calls, and the piece and ready words count the calls."""
+def test_background_reduce_integer_exact_repeated():
+    """Integer inputs give the oracle's results exactly on each of three
+    calls, and the piece and ready words count the calls."""
     w = gen.WORKLOADS["comm_dominant"]
     A, B, peers = gen.make_inputs(w, DEV, seed=64, integer=True)
     res = orc.gemm_rs_oracle(gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers), w.P,
                              w.rank, w.chunk_rows)
     share = H.Share(w, "f32")
-    _, pieces, err = _side(w)
-    call = pk.BoundInterCUReduce(A, B, peers, share.send, share.out, share.flags, share.out,
+    presum, pieces, err = _side(w)
+    call = pk.BoundInterCUReduce(A, B, peers, share.send, share.out, share.flags, presum,
                                  pieces, err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows,
                                  w.tile_order, 0, 1, 0)
     half = share.flags.numel() // 2
     for n in (1, 2, 3):
         call()
-        torch.cuda.synchronize()
+        assert call.check() == 0
         assert np.array_equal(gen.bf16_bits(share.send), res.send_bits)
         assert np.array_equal(share.out.cpu().numpy().astype(np.float64), res.out)
         assert int(share.flags[:half].min()) == n and int(share.flags[:half].max()) == n
@@ -338,14 +353,13 @@ def test_background_reduce_incoming_chunk_waits():
 
 def test_background_reduce_piece_wait_gives_up():
     """Owned tiles told to wait for call 5 while the pieces reach 1 give up
-    (error bit 1); presum already holds this call's sums, and the send
-    workgroups write the same bits, so the results are the staged share's."""
+    (error bit 1) and sum their staged peers themselves: presum is NaN-filled
+    when the launch starts, yet the results are the staged share's."""
     w = gen.WORKLOADS["comm_dominant"]
     A, B, peers = gen.make_inputs(w, DEV, seed=66)
     ref = H.Share(w, "f32")
     H.run(ref, A, B, peers)
     presum, pieces, err = _side(w)
-    presum.copy_(_peer_sum_f32(peers))
     share = H.Share(w, "f32")
     pk.pk_gemm_rs_intercu_reduce(A, B, peers, share.send, share.out, share.flags, presum, pieces,
                                  err, w.M, w.N, w.K, w.P, w.rank, w.chunk_rows, w.tile_order, 0,
@@ -369,6 +383,11 @@ def test_background_reduce_rejects_what_it_cannot_run():
         with pytest.raises(pk.PkError) as e:
             pk.pk_gemm_rs_intercu_reduce(*args, **kw)
         assert e.value.code == -5
+    # presum may not be out itself here: a send tile's workgroup that started
+    # late would store its bare peer sum over a finished owned tile
+    with pytest.raises(pk.PkError) as e:
+        pk.pk_gemm_rs_intercu_reduce(*args[:6], share.out, *args[7:])
+    assert e.value.code == -1
     w4 = gen.WORKLOADS["comm_dominant"].with_(P=4, rank=1)
     A4, B4, p4 = gen.make_inputs(w4, DEV, seed=68)
     s4 = H.Share(w4, "f32")
