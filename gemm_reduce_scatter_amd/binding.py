@@ -113,6 +113,13 @@ def load():
     lib.pk_gemm_rs_intercu_reduce.restype = i32
     lib.pk_reduce_piece_words.argtypes = [i64, i64, i32]
     lib.pk_reduce_piece_words.restype = i64
+    lib.pk_gemm_rs_intercu_reduce_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                                     i64, i32, i32, i32, i32, i32,
+                                                     ctypes.c_uint32, i32, i32,
+                                                     ctypes.POINTER(_Options), vp]
+    lib.pk_gemm_rs_intercu_reduce_static.restype = i32
+    lib.pk_static_workspace_limits.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.pk_static_workspace_limits.restype = i64
     del u32p
     _lib = lib
     return lib
@@ -499,6 +506,71 @@ def _check_reduce_error(e: int, presum_is_out: bool) -> int:
         raise IncompleteError(f"reduction role gave up waits (error word {e}): out is not valid",
                               np.array([e], np.int32))
     return int(e)
+
+
+class BoundInterCUReduceStatic:
+    """pk_gemm_rs_intercu_reduce_static (workspace in the library's static
+    device array) with its arguments checked and marshalled once; calling the
+    object launches with `expected` for the incoming chunk words."""
+
+    def __init__(self, A, B, peer_partials, send_bufs, out, flags, error, M, N, K, P, rank,
+                 chunk_rows, tile_order, out_bf16, expected=0, num_comm_cus=0,
+                 spin_limit=1 << 16, peer_ready=None, config=0, max_workgroups=0, group_n=0,
+                 owned_split=0, signal_batch=0, store_policy=0, stream=None):
+        import torch
+        _check_tensors(A, B, peer_partials, send_bufs, out, flags)
+        _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
+                     out_bf16)
+        for name, t in (("error", error), ("peer_ready", peer_ready)):
+            if t is None:
+                if name == "error":
+                    raise ValueError("error is required")
+                continue
+            if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.int32,
+                                                                          torch.uint32):
+                raise ValueError(f"{name} must be a contiguous 32-bit integer device tensor")
+        if error.numel() < 1:
+            raise ValueError("error needs one word")
+        n = _chunks(M, P, chunk_rows)
+        if peer_ready is not None and n > 0 and peer_ready.numel() < n:
+            raise ValueError("peer_ready needs one word per incoming chunk")
+        self._keep = (A, B, peer_partials, send_bufs, out, flags, error, peer_ready)
+        self._opts = _opts(config, max_workgroups, group_n, False, owned_split, signal_batch,
+                           store_policy=store_policy)
+        self._fn = load().pk_gemm_rs_intercu_reduce_static
+        self._head = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(peer_ready), _ptr(send_bufs),
+                      _ptr(out), _ptr(flags), _ptr(error), int(M), int(N), int(K), int(P),
+                      int(rank), int(chunk_rows), int(tile_order), int(out_bf16))
+        self._tail = (int(num_comm_cus), int(spin_limit), ctypes.byref(self._opts),
+                      _stream(stream))
+        self.expected = int(expected)
+
+    def __call__(self) -> int:
+        return _check(self._fn(*self._head, ctypes.c_uint32(self.expected & 0xFFFFFFFF),
+                               *self._tail))
+
+    def check(self, stream=None) -> int:
+        """The error word after the launches so far (see BoundInterCUReduce.check)."""
+        return _check_reduce_error(read_words(self._keep[6], stream)[0], False)
+
+
+def pk_gemm_rs_intercu_reduce_static(A, B, peer_partials, send_bufs, out, flags, error, M, N, K,
+                                     P, rank, chunk_rows, tile_order, out_bf16, expected=0,
+                                     num_comm_cus=0, spin_limit=1 << 16, peer_ready=None,
+                                     stream=None, **opts) -> int:
+    """The reduction role with its workspace in the library's static device
+    array, for callers that cannot allocate (see pk_gemm_rs.h)."""
+    return BoundInterCUReduceStatic(A, B, peer_partials, send_bufs, out, flags, error, M, N, K,
+                                    P, rank, chunk_rows, tile_order, out_bf16, expected,
+                                    num_comm_cus, spin_limit, peer_ready, stream=stream,
+                                    **opts)()
+
+
+def pk_static_workspace_limits():
+    """(max (M/P)*N, max piece words, bytes per GPU) of the static workspace."""
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    nbytes = load().pk_static_workspace_limits(ctypes.byref(a), ctypes.byref(b))
+    return int(a.value), int(b.value), int(nbytes)
 
 
 def pk_gemm_rs_intercu_reduce(A, B, peer_partials, send_bufs, out, flags, presum, piece_ready,

@@ -1849,6 +1849,36 @@ static int validate_reduce(const void* A, const void* B, const void* peers, cons
   return PK_OK;
 }
 
+// Workspace of pk_gemm_rs_intercu_reduce_static, for callers that cannot
+// allocate: the fp32 peer sum of the owned shard (at most kScratchSums
+// elements, 16 MiB) followed by the piece words (at most kScratchPieces).
+// One copy per GPU, held until the process ends; calls on one GPU share it.
+constexpr long long kScratchSums = 1LL << 22;
+constexpr long long kScratchPieces = 1LL << 16;
+__device__ __align__(256) unsigned char scratch[(kScratchSums + kScratchPieces) * 4];
+
+// The device address of this GPU's copy of `scratch`, looked up once per
+// device with that device current (host code must never pass the array's
+// name itself to a kernel: on the host it is only a stand-in).
+static unsigned char* scratch_ptr(int dev) {
+  static unsigned char* ptr[64];
+  static hipError_t err[64];
+  static std::once_flag once[64];
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::call_once(once[dev], [&] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    ptr[dev] = err[dev] == hipSuccess ? static_cast<unsigned char*>(p) : nullptr;
+  });
+  return ptr[dev];
+}
+
+// Sets n words to v (a kernel, not a memset, so the call can be captured in a
+// graph).
+__global__ void __launch_bounds__(256) fill_words(uint32_t* p, long long n, uint32_t v) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += gridDim.x * 256LL) p[i] = v;
+}
+
 }  // namespace pk
 
 // ---------------------------------------------------------------------------
@@ -1942,6 +1972,42 @@ int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_par
   const int n_comm = (num_comm_cus + 7) / 8 * 8;   // whole XCD rounds
   return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
                  tile_order, out_bf16, opts, stream, false, n_comm, nullptr, &red);
+}
+
+int pk_gemm_rs_intercu_reduce_static(const void* A, const void* B, const void* peer_partials,
+                                     const uint32_t* peer_ready, void* send_bufs, void* out,
+                                     uint32_t* flags, int32_t* error, int64_t M, int64_t N,
+                                     int64_t K, int P, int rank, int chunk_rows, int tile_order,
+                                     int out_bf16, uint32_t expected, int num_comm_cus,
+                                     int spin_limit, const pk_options* opts, void* stream) {
+  const int v = pk::validate_reduce(A, B, peer_partials, peer_ready, send_bufs, out, flags, error,
+                                    M, N, K, P, rank, chunk_rows, tile_order, out_bf16,
+                                    num_comm_cus, spin_limit, opts);
+  if (v != PK_OK || M == 0 || N == 0) return v;
+  const long long S = M / P;
+  const long long pieces = ((S + pk::kPiece - 1) / pk::kPiece) * ((N + pk::kPiece - 1) / pk::kPiece);
+  if (S * N > pk::kScratchSums || pieces > pk::kScratchPieces) return PK_ERR_SCRATCH;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_LAUNCH;
+  unsigned char* ws = pk::scratch_ptr(dev);
+  if (ws == nullptr) return PK_ERR_LAUNCH;
+  float* presum = reinterpret_cast<float*>(ws);
+  uint32_t* piece_ready = reinterpret_cast<uint32_t*>(ws + pk::kScratchSums * 4);
+  // the words keep the last call's counts: start this call's from zero
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned blocks = (unsigned)((pieces + 255) / 256);
+  hipLaunchKernelGGL(pk::fill_words, dim3(blocks), dim3(256), 0, s, piece_ready, pieces, 0u);
+  if (hipGetLastError() != hipSuccess) return PK_ERR_LAUNCH;
+  pk::RedArgs red{presum, piece_ready, peer_ready, error, expected, 1u, spin_limit};
+  const int n_comm = (num_comm_cus + 7) / 8 * 8;   // whole XCD rounds
+  return pk::run(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank, chunk_rows,
+                 tile_order, out_bf16, opts, stream, false, n_comm, nullptr, &red);
+}
+
+int64_t pk_static_workspace_limits(int64_t* max_sum_elements, int64_t* max_piece_words) {
+  if (max_sum_elements) *max_sum_elements = pk::kScratchSums;
+  if (max_piece_words) *max_piece_words = pk::kScratchPieces;
+  return (pk::kScratchSums + pk::kScratchPieces) * 4;
 }
 
 int64_t pk_reduce_piece_words(int64_t M, int64_t N, int P) {
@@ -2059,6 +2125,7 @@ const char* pk_strerror(int code) {
     case PK_ERR_CONFIG: return "unknown tile configuration or option";
     case PK_ERR_LAUNCH: return "HIP launch failed";
     case PK_ERR_TOO_LARGE: return "dimension exceeds 2^31";
+    case PK_ERR_SCRATCH: return "shape needs more than the static workspace holds (pk_static_workspace_limits)";
     default: return "unknown error";
   }
 }

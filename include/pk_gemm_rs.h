@@ -68,6 +68,7 @@ extern "C" {
 #define PK_ERR_CONFIG (-5)      /* requested tile configuration does not exist */
 #define PK_ERR_LAUNCH (-6)      /* the HIP runtime refused the launch */
 #define PK_ERR_TOO_LARGE (-7)   /* a buffer exceeds the 32-bit element offsets used */
+#define PK_ERR_SCRATCH (-8)     /* the shape needs more than the static workspace holds */
 
 #define PK_TILE_ROW_MAJOR 0       /* shards 0..P-1 in order, chunk-major inside */
 #define PK_TILE_OWNED_FIRST 1     /* owned shard, then rank+1, rank+2, ... (mod P) */
@@ -238,6 +239,32 @@ int pk_gemm_rs_intercu_reduce(const void* A, const void* B, const void* peer_par
 /* Number of piece words pk_gemm_rs_intercu_reduce reads and raises:
  * ceil((M/P)/64) * ceil(N/64), or a negative PK_ERR_* code. */
 int64_t pk_reduce_piece_words(int64_t M, int64_t N, int P);
+
+/* pk_gemm_rs_intercu_reduce without a caller-provided workspace, for callers
+ * that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid it): the fp32 peer sum and the piece
+ * words live in a static array of this library, one copy per GPU held until
+ * the process ends (pk_static_workspace_limits gives its size).  Arguments,
+ * outputs, error bits and the background mode (num_comm_cus = 0) are those
+ * of pk_gemm_rs_intercu_reduce, with presum a separate buffer; `expected`
+ * applies to the incoming chunk words (peer_ready) only, the piece words are
+ * cleared by each call and raised once.  The call allocates nothing: it runs
+ * a small fill kernel and the fused kernel on `stream`.  Shapes with
+ * (M/P) * N above max_sum_elements or more piece words than max_piece_words
+ * return PK_ERR_SCRATCH.  Every call on one GPU uses the same workspace: two
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and their results are undefined; calls in one stream are ordered and safe. */
+int pk_gemm_rs_intercu_reduce_static(const void* A, const void* B, const void* peer_partials,
+                                     const uint32_t* peer_ready, void* send_bufs, void* out,
+                                     uint32_t* flags, int32_t* error, int64_t M, int64_t N,
+                                     int64_t K, int P, int rank, int chunk_rows, int tile_order,
+                                     int out_bf16, uint32_t expected, int num_comm_cus,
+                                     int spin_limit, const pk_options* opts, void* stream);
+
+/* Capacity of the static workspace of pk_gemm_rs_intercu_reduce_static:
+ * writes the largest (M/P) * N and piece-word count it accepts (either
+ * pointer may be NULL) and returns the workspace's size in bytes per GPU. */
+int64_t pk_static_workspace_limits(int64_t* max_sum_elements, int64_t* max_piece_words);
 
 /* All-gather + GEMM, the step before the reduce-scatter in a tensor-
  * parallel MLP (ParallelKittens summary page, "Data and Tensor Parallelism:
