@@ -118,16 +118,20 @@ def _draw(shape, dist: str, K: int, device, seed: int) -> torch.Tensor:
     raise ValueError(f"unknown distribution {dist!r}")
 
 
-def make_inputs(w: Workload, device="cpu", seed: int = 0, integer: bool = False):
-    """A [M,K], B [K,N], peers [P-1,S,N] as bf16 tensors on ``device``."""
+def make_operands(w: Workload, device="cpu", seed: int = 0, integer: bool = False):
+    """A [M,K] and B [K,N] only: the same bytes make_inputs draws for them."""
     ab = "int5" if integer else w.ab_dist
-    pd = "int17" if integer else w.peer_dist
     if ab == "int":
         ab = "int5"
+    return _draw((w.M, w.K), ab, w.K, device, seed), _draw((w.K, w.N), ab, w.K, device, seed + 1)
+
+
+def make_inputs(w: Workload, device="cpu", seed: int = 0, integer: bool = False):
+    """A [M,K], B [K,N], peers [P-1,S,N] as bf16 tensors on ``device``."""
+    pd = "int17" if integer else w.peer_dist
     if pd == "int":
         pd = "int17"
-    A = _draw((w.M, w.K), ab, w.K, device, seed)
-    B = _draw((w.K, w.N), ab, w.K, device, seed + 1)
+    A, B = make_operands(w, device, seed, integer)
     peers = torch.empty((max(w.P - 1, 0), w.S, w.N), dtype=torch.bfloat16, device=device)
     for j in range(w.P - 1):
         peers[j] = _draw((w.S, w.N), pd, w.K, device, seed + 2 + j)

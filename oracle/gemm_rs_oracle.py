@@ -73,6 +73,8 @@ __all__ = [
     "reduce_scatter_share",
     "gemm_rs_oracle",
     "gemm_rs_elements",
+    "partial_elements",
+    "owned_elements",
     "error_bound",
     "OracleResult",
     "consume_chunks",
@@ -260,6 +262,36 @@ def gemm_rs_oracle(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits: np.ndarray
     C = local_partial(A_bits, B_bits)
     peers = bf16_bits_to_f64(peer_bits)
     return reduce_scatter_share(C, peers, P, rank, chunk_rows, ready_before)
+
+
+def partial_elements(A_rows_bits: np.ndarray, B_cols_bits: np.ndarray):
+    """C at paired positions: element i is row i of ``A_rows_bits`` [n, K]
+    (bf16 bits) dotted with column i of ``B_cols_bits`` [K, n].
+
+    [PKN] section 3: one element of the local partial C = A . B, each its own
+    fp64 dot product (the products of two bf16 numbers are exact in fp64).
+    Returns (value, |A|.|B|) per position.
+    """
+    A = bf16_bits_to_f64(np.asarray(A_rows_bits))
+    B = bf16_bits_to_f64(np.asarray(B_cols_bits)).T
+    if A.shape != B.shape:
+        raise ValueError("need A rows [n, K] and B columns [K, n]")
+    return np.einsum("ik,ik->i", A, B), np.einsum("ik,ik->i", np.abs(A), np.abs(B))
+
+
+def owned_elements(c_val: np.ndarray, c_mag: np.ndarray, peer_bits_at: np.ndarray):
+    """Owned-shard values at sampled positions: [PK] "Scheduling Analysis",
+    the owner's result is its own partial plus every peer's, here
+    C + sum_j peers[j] in ascending slot order (fp64).  ``peer_bits_at`` is
+    [P-1, n], the bf16 bits of each slot at the positions.  Returns
+    (value, |A|.|B| + sum_j |peer_j|)."""
+    val = np.array(c_val, dtype=np.float64, copy=True)
+    mag = np.array(c_mag, dtype=np.float64, copy=True)
+    for j in range(np.asarray(peer_bits_at).shape[0]):
+        pv = bf16_bits_to_f64(np.asarray(peer_bits_at)[j])
+        val = val + pv
+        mag = mag + np.abs(pv)
+    return val, mag
 
 
 def gemm_rs_elements(A_bits: np.ndarray, B_bits: np.ndarray, peer_bits, P: int,

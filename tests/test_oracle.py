@@ -392,6 +392,39 @@ def test_local_partial_abs_by_hand():
                           orc.local_partial(_bits(np.abs(Ar)), _bits(np.abs(Br))))
 
 
+def test_partial_and_owned_elements_match_the_full_share():
+    # the paired-position functions against the full product (local_partial,
+    # pinned above) and the full share (reduce_scatter_share)
+    w = gen.WORKLOADS["tiny"].with_(P=4, rank=1, M=32, N=24, K=40, chunk_rows=4)
+    A, B, peers = gen.make_inputs(w, seed=6)
+    Ab, Bb, Pb = gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers)
+    full = orc.gemm_rs_oracle(Ab, Bb, Pb, w.P, w.rank, w.chunk_rows)
+    T = orc.local_partial_abs(Ab, Bb)
+    rng = np.random.default_rng(2)
+    rows = rng.integers(0, w.M, 300)
+    cols = rng.integers(0, w.N, 300)
+    val, mag = orc.partial_elements(Ab[rows], Bb[:, cols])
+    np.testing.assert_allclose(val, full.C[rows, cols], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(mag, T[rows, cols], rtol=1e-13, atol=0)
+    S = w.S
+    own = (rows // S) == w.rank
+    lr, lc = rows[own] - w.rank * S, cols[own]
+    ov, om = orc.owned_elements(val[own], mag[own], Pb[:, lr, lc])
+    np.testing.assert_allclose(ov, full.out[lr, lc], rtol=1e-13, atol=1e-13)
+    pabs = np.sum(np.abs(orc.bf16_bits_to_f64(Pb)), axis=0)
+    np.testing.assert_allclose(om, T[rows[own], lc] + pabs[lr, lc], rtol=1e-13, atol=0)
+    # integer twin: exact
+    Ai, Bi, Pi = gen.make_inputs(w, seed=7, integer=True)
+    Ab, Bb, Pb = gen.bf16_bits(Ai), gen.bf16_bits(Bi), gen.bf16_bits(Pi)
+    full = orc.gemm_rs_oracle(Ab, Bb, Pb, w.P, w.rank, w.chunk_rows)
+    val, _ = orc.partial_elements(Ab[rows], Bb[:, cols])
+    assert np.array_equal(val, full.C[rows, cols])
+    ov, _ = orc.owned_elements(val[own], mag[own], Pb[:, lr, lc])
+    assert np.array_equal(ov, full.out[lr, lc])
+    with pytest.raises(ValueError):
+        orc.partial_elements(Ab[rows[:3]], Bb[:, cols[:4]])
+
+
 def test_sampled_magnitudes_are_abs_products_plus_peer_magnitudes():
     w = gen.WORKLOADS["tiny"].with_(P=4, rank=2, M=32, N=16, K=24, chunk_rows=4)
     A, B, peers = gen.make_inputs(w, seed=5)
