@@ -71,6 +71,9 @@ def parse():
                    help="skip the inter-CU reduction role beside the staged share")
     p.add_argument("--sweep", action="store_true",
                    help="large-K schedule sweep: chunk_rows x tile order, one JSON line each")
+    p.add_argument("--timeline", action="store_true",
+                   help="phase times and CU placement of every workgroup, from the "
+                        "instrumented timing build (libpk_gemm_rs_timeline.so); one JSON line")
     return p.parse_args()
 
 
@@ -378,6 +381,87 @@ def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
                                 "min": round(float(lat.min()), 2)}}
 
 
+def timeline_study(w, args, torch, gen, pk):
+    """Per-workgroup phase record of the timing build of the library (the
+    same sources compiled with PK_TIMELINE): each workgroup's CU placement
+    and the 100 MHz device clock at each phase boundary (1 first stage
+    landed, 2 main loop done, 3 epilogue done, 4 ready words raised), over
+    `steps` launches back to back on rotating buffer sets.  Workgroups are
+    grouped by their sequence of phases (their role in the schedule); the
+    line reports the median time of each phase from the launch's first
+    workgroup start, and how the workgroups shared the CUs."""
+    import numpy as np
+    pk.use_library(pk.TIMELINE_LIB_NAME)
+    chunk = args.chunk_rows or w.chunk_rows
+    order = w.tile_order if args.tile_order is None else args.tile_order
+    set_bytes = w.algorithmic_bytes()
+    n_sets = max(2, min(8, math.ceil(1.2 * MALL_BYTES / set_bytes))) if set_bytes < 2 * MALL_BYTES else 1
+    sets = [BufferSet(w, 17 * i, chunk, torch, gen, pk) for i in range(n_sets)]
+    out_bf16 = 1 if w.out_dtype == "bf16" else 0
+    opts = dict(config=args.config, max_workgroups=args.max_workgroups, group_n=args.group_n,
+                store_policy=args.store_policy, owned_split=args.owned_split)
+    words = pk.TIMELINE_BYTES // 8
+    tls = [torch.zeros(words, dtype=torch.int64, device="cuda") for _ in range(args.steps)]
+    scratch = torch.zeros(words, dtype=torch.int64, device="cuda")
+
+    def call(i, tl):
+        s = sets[i % n_sets]
+        return pk.BoundCall(s.A, s.B, s.peers, s.send, s.out, s.flags, w.M, w.N, w.K, w.P, w.rank,
+                            chunk, order, out_bf16, timeline=tl, **opts)
+    warm = [call(i, scratch) for i in range(n_sets)]
+    for i in range(args.warmup):
+        warm[i % n_sets]()
+    steps = [call(args.warmup + i, tls[i]) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    for c in steps:
+        c()
+    torch.cuda.synchronize()
+    groups = {}
+    spans, placement = [], None
+    mask56 = (1 << 56) - 1
+    for tl in tls:
+        t = tl.cpu().numpy().view(np.uint64).reshape(pk.TIMELINE_WORKGROUPS, pk.TIMELINE_SLOTS)
+        live = np.nonzero(t[:, 1])[0]
+        t0 = int(t[live, 1].min())
+        end = t0
+        for b in live:
+            marks = [int(m) for m in t[b, 2:] if m]
+            kinds = tuple(m >> 56 for m in marks)
+            times = [((m & mask56) - t0) / 100.0 for m in marks]
+            g = groups.setdefault(kinds, {"workgroups": 0, "start": [], "times": []})
+            g["workgroups"] += 1
+            g["start"].append((int(t[b, 1]) - t0) / 100.0)
+            g["times"].append(times)
+            if marks:
+                end = max(end, marks[-1] & mask56)
+        spans.append((end - t0) / 100.0)
+        if placement is None:
+            hw = t[live, 0]
+            cu = [(int(h >> 32), int((h >> 13) & 7), int((h >> 8) & 15)) for h in hw]
+            per_cu = {}
+            for b, c in zip(live, cu):
+                per_cu.setdefault(c, []).append(int(b))
+            grid = len(live)
+            mixed = sum(1 for v in per_cu.values()
+                        if any(b < grid // 2 for b in v) and any(b >= grid // 2 for b in v))
+            placement = {"workgroups": grid, "cus_used": len(per_cu),
+                         "workgroups_per_cu": {str(k): sum(1 for v in per_cu.values() if len(v) == k)
+                                               for k in sorted({len(v) for v in per_cu.values()})},
+                         "cus_with_both_halves": mixed}
+    roles = []
+    names = {1: "stage", 2: "main", 3: "epilogue", 4: "signal"}
+    for kinds, g in sorted(groups.items(), key=lambda kv: -kv[1]["workgroups"]):
+        med = np.median(np.array(g["times"]), axis=0) if g["times"] and kinds else []
+        roles.append({"phases": "-".join(names.get(k, str(k)) for k in kinds),
+                      "workgroups_per_launch": round(g["workgroups"] / len(tls), 1),
+                      "start_us": round(float(np.median(g["start"])), 2),
+                      "phase_end_us": [round(float(x), 2) for x in med]})
+    pk.use_library(pk.LIB_NAME)
+    return {"workload": w.name, "config": args.config, "launches": len(tls),
+            "span_us_median": round(float(np.median(spans)), 2), "placement": placement,
+            "roles": roles}
+
+
 def source_digest():
     """sha256 over the HIP sources of the library (the kernel the counters saw)."""
     d = os.path.join(ROOT, "gemm_reduce_scatter_amd", "csrc")
@@ -479,6 +563,9 @@ def main():
         return
     pk.load()
     w = gen.WORKLOADS[args.workload]
+    if args.timeline:
+        print(json.dumps(timeline_study(w, args, torch, gen, pk)), flush=True)
+        return
     if args.sweep:
         w = gen.WORKLOADS["large_k"]
         for chunk in w.sweep_chunk_rows:

@@ -49,11 +49,15 @@ class _Options(ctypes.Structure):
     _fields_ = [("config", ctypes.c_int), ("max_workgroups", ctypes.c_int),
                 ("group_n", ctypes.c_int), ("gemm_only", ctypes.c_int),
                 ("owned_split", ctypes.c_int), ("signal_batch", ctypes.c_int),
-                ("ready_clock", ctypes.c_void_p), ("store_policy", ctypes.c_int)]
+                ("ready_clock", ctypes.c_void_p), ("store_policy", ctypes.c_int),
+                ("timeline", ctypes.c_void_p)]
 
 
-def lib_path() -> str:
-    return os.path.join(_HERE, LIB_NAME)
+TIMELINE_LIB_NAME = "libpk_gemm_rs_timeline.so"
+
+
+def lib_path(name: str = LIB_NAME) -> str:
+    return os.path.join(_HERE, name)
 
 
 def load():
@@ -61,7 +65,20 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
-    path = lib_path()
+    _lib = _open(lib_path())
+    return _lib
+
+
+def use_library(name: str = LIB_NAME):
+    """Make every call below go to the library `name` in the package
+    directory: LIB_NAME (the product) or TIMELINE_LIB_NAME (the same sources
+    built with the phase recorder, for timing studies).  Returns it."""
+    global _lib
+    _lib = _open(lib_path(name))
+    return _lib
+
+
+def _open(path: str):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: run __graft_entry__.build() (hipcc, gfx950) first")
     lib = ctypes.CDLL(path)
@@ -121,7 +138,6 @@ def load():
     lib.pk_static_workspace_limits.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.pk_static_workspace_limits.restype = i64
     del u32p
-    _lib = lib
     return lib
 
 
@@ -151,10 +167,19 @@ def _stream(stream):
 
 
 def _opts(config=0, max_workgroups=0, group_n=0, gemm_only=False, owned_split=0,
-          signal_batch=0, ready_clock=None, store_policy=0):
+          signal_batch=0, ready_clock=None, store_policy=0, timeline=None):
+    if timeline is not None and (timeline.numel() * timeline.element_size() < TIMELINE_BYTES
+                                 or not timeline.is_contiguous()):
+        raise ValueError(f"timeline must be a contiguous buffer of {TIMELINE_BYTES} bytes")
     return _Options(int(config), int(max_workgroups), int(group_n), 1 if gemm_only else 0,
                     int(owned_split), int(signal_batch),
-                    None if ready_clock is None else ready_clock.data_ptr(), int(store_policy))
+                    None if ready_clock is None else ready_clock.data_ptr(), int(store_policy),
+                    None if timeline is None else timeline.data_ptr())
+
+
+# Phase record of the instrumented timing build: 2048 workgroups x 32 uint64.
+TIMELINE_WORKGROUPS, TIMELINE_SLOTS = 2048, 32
+TIMELINE_BYTES = TIMELINE_WORKGROUPS * TIMELINE_SLOTS * 8
 
 
 def _check_tensors(A, B, peer_partials, send_bufs, out, flags):
@@ -225,17 +250,19 @@ def pk_gemm_rs_local_bf16out(A, B, peer_partials, send_bufs, out, flags, M, N, K
 def pk_gemm_rs_local_ex(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                         chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0,
                         group_n=0, gemm_only=False, owned_split=0, signal_batch=0,
-                        ready_clock=None, store_policy=0, stream=None) -> int:
+                        ready_clock=None, store_policy=0, timeline=None, stream=None) -> int:
     """Fused share with explicit tile configuration / grid / grouping options.
 
     ready_clock: None or a device int64 tensor of (P-1)*S/chunk_rows words that
-    receives the device clock at which each chunk's ready word rose."""
+    receives the device clock at which each chunk's ready word rose.
+    timeline: None or a device buffer of TIMELINE_BYTES, filled only by the
+    instrumented timing build (see use_library)."""
     _check_tensors(A, B, peer_partials, send_bufs, out, flags)
     _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows, out_bf16,
                  gemm_only)
     _check_clock(ready_clock, M, P, chunk_rows, gemm_only)
     o = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch, ready_clock,
-              store_policy)
+              store_policy, timeline)
     return _check(load().pk_gemm_rs_local_ex(
         _ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out), _ptr(flags),
         int(M), int(N), int(K), int(P), int(rank), int(chunk_rows), int(tile_order),
@@ -627,14 +654,14 @@ class BoundCall:
     def __init__(self, A, B, peer_partials, send_bufs, out, flags, M, N, K, P, rank,
                  chunk_rows, tile_order, out_bf16, config=0, max_workgroups=0, group_n=0,
                  gemm_only=False, owned_split=0, signal_batch=0, ready_clock=None,
-                 store_policy=0, stream=None):
+                 store_policy=0, timeline=None, stream=None):
         _check_tensors(A, B, peer_partials, send_bufs, out, flags)
         _check_sizes(A, B, peer_partials, send_bufs, out, flags, M, N, K, P, chunk_rows,
                      out_bf16, gemm_only)
         _check_clock(ready_clock, M, P, chunk_rows, gemm_only)
-        self._keep = (A, B, peer_partials, send_bufs, out, flags, ready_clock)
+        self._keep = (A, B, peer_partials, send_bufs, out, flags, ready_clock, timeline)
         self._opts = _opts(config, max_workgroups, group_n, gemm_only, owned_split, signal_batch,
-                           ready_clock, store_policy)
+                           ready_clock, store_policy, timeline)
         self._fn = load().pk_gemm_rs_local_ex
         self._args = (_ptr(A), _ptr(B), _ptr(peer_partials), _ptr(send_bufs), _ptr(out),
                       _ptr(flags), int(M), int(N), int(K), int(P), int(rank), int(chunk_rows),

@@ -55,9 +55,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // WAVES_M x WAVES_N arrangement; each wave owns a WM x WN block of 32x32
 // MFMA accumulators.  STAGES-deep ring of LDS operand buffers of BK k each.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int OCC_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int OCC = OCC_;   // workgroups meant to share a CU
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = WAVES * 64;
@@ -93,17 +94,31 @@ struct Cfg {
   static_assert(A_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0, "A stage splits over the waves");
   static_assert(B_LOADS >= 1 && B_BYTES % (1024 * WAVES) == 0, "B stage splits over the waves");
   static_assert(B_CPR >= 8 && B_CPR <= 64, "B row is 8..64 chunks");
-  static_assert(LDS <= 160 * 1024, "fits the 160 KiB LDS of a CU");
+  static_assert(LDS * OCC <= 160 * 1024, "fits the 160 KiB LDS of a CU");
 };
 
-// id 1..5; the table in pk_config_info mirrors these.
+// id 1..6; the table in pk_config_info mirrors these.
 using Cfg1 = Cfg<256, 256, 2, 2, 32, 4>;
 using Cfg2 = Cfg<128, 128, 2, 2, 64, 2>;
 using Cfg3 = Cfg<64, 64, 2, 2, 64, 2>;
 using Cfg4 = Cfg<256, 128, 2, 2, 32, 4>;
 using Cfg5 = Cfg<256, 256, 2, 2, 64, 2>;
-// Owned sub-tiles of Cfg1 tiles when the owned shard is split (8 per tile).
+// Two workgroups per CU: 72 KiB of LDS and at most 256 registers per lane
+// each (128 accumulators), so one workgroup's stores and latency-bound steps
+// overlap the other's MFMAs.
+using Cfg6 = Cfg<256, 128, 2, 2, 32, 3, 2>;
+// Owned sub-tiles when the owned shard is split: 64 x 128, eight per Cfg1
+// tile, four per Cfg6 tile (with that configuration's LDS budget).
 using CfgOwned = Cfg<64, 128, 2, 2, 64, 4>;
+using CfgOwned3 = Cfg<64, 128, 2, 2, 64, 3, 2>;
+template <class C>
+struct OwnedOf {
+  using type = CfgOwned;
+};
+template <>
+struct OwnedOf<Cfg6> {
+  using type = CfgOwned3;
+};
 
 struct KArgs {
   const uint16_t* A;
@@ -141,7 +156,46 @@ struct KArgs {
   const uint32_t* peer_ready;
   Grid g;
   long long total_tiles;
+  uint64_t* timeline;   // null, or the phase record of an instrumented build
 };
+
+// Instrumented timing build (compiled with -DPK_TIMELINE, a library of its
+// own; the product library has no trace of it): thread 0 of every workgroup
+// writes into timeline[blockIdx][kTlSlots] its hardware placement (slot 0:
+// XCC id << 32 | the HW_ID register: CU, SE, SIMD), the 100 MHz wall clock at
+// its start (slot 1) and, in later slots, (kind << 56) | clock at each phase
+// boundary: 1 first stage landed, 2 main loop done, 3 epilogue done, 4 ready
+// words raised.  Nothing else changes: the results are bitwise the product
+// library's.
+constexpr int kTlSlots = 32;
+constexpr long long kTimelineWorkgroups = 2048;   // the record holds this many workgroups
+#ifdef PK_TIMELINE
+__device__ __forceinline__ int& tl_slot() {
+  __shared__ int n;
+  return n;
+}
+__device__ __forceinline__ void tl_start(const KArgs& a) {
+  if (a.timeline && threadIdx.x == 0) {
+    tl_slot() = 2;
+    const uint64_t hw = (uint64_t)__builtin_amdgcn_s_getreg((31 << 11) | 4) |
+                        ((uint64_t)__builtin_amdgcn_s_getreg((3 << 11) | 20) << 32);
+    a.timeline[(long long)blockIdx.x * kTlSlots] = hw;
+    a.timeline[(long long)blockIdx.x * kTlSlots + 1] = wall_clock64();
+  }
+}
+__device__ __forceinline__ void tl_mark(const KArgs& a, uint64_t kind) {
+  if (a.timeline && threadIdx.x == 0) {
+    int& n = tl_slot();
+    if (n < kTlSlots) a.timeline[(long long)blockIdx.x * kTlSlots + n] = (kind << 56) | wall_clock64();
+    ++n;
+  }
+}
+#define PK_TL_START(a) tl_start(a)
+#define PK_MARK(a, kind) tl_mark(a, kind)
+#else
+#define PK_TL_START(a) ((void)0)
+#define PK_MARK(a, kind) ((void)0)
+#endif
 
 // LDS swizzles.  A: the 16 rows a 16-lane group reads at one logical chunk
 // land in 16 distinct 16-byte bank groups, and so do the 8 rows of each
@@ -720,9 +774,11 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
   float* stage = lds_f + wave * 16 * C::EPI_STRIDE;
   constexpr int LPR = SG::LPR, RPI = SG::RPI, PASSES = SG::PASSES;
   // owned segments summed together: 4 for small wave tiles, 2 when the
-  // accumulators take a large part of the register file
-  constexpr int BATCH =
-      SRC != kPeersDirect ? PASSES : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
+  // accumulators take a large part of the register file, 1 when two
+  // workgroups share the CU's registers
+  constexpr int BATCH = SRC != kPeersDirect ? PASSES
+                        : C::OCC > 1        ? 1
+                        : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
   static_assert(PASSES % BATCH == 0, "batches tile the passes");
   const bool owned = staged_mode(MODE) && shard == a.rank;
   const int c8 = lane % LPR;
@@ -938,7 +994,7 @@ struct LdsPlan {
   static constexpr int ST = mx(C1::STAGES, C2::STAGES);
   static constexpr int B2 = ST > 2 ? BS : 16;
   static constexpr int B3 = ST > 3 ? BS : 16;
-  static_assert(B0 + BS + B2 + B3 <= 160 * 1024, "fits the 160 KiB LDS of a CU");
+  static_assert((B0 + BS + B2 + B3) * C1::OCC <= 160 * 1024, "fits the 160 KiB LDS of a CU");
 };
 
 // Main loop of one work item: a tile of configuration C whose first row is
@@ -984,6 +1040,7 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    PK_MARK(a, 1);
   }
   typename Reader<C>::Frags f[2];
   if (nk > 0) rd.read(b0, 0, f[0]);
@@ -1011,6 +1068,7 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
     __syncthreads();
   }
   bg.finish(a);
+  PK_MARK(a, 2);
 }
 
 // One work item: its main loop (main_part), then its epilogue.  An owned
@@ -1043,6 +1101,7 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   }
   epilogue<C, MODE, GS, SRC, PVT>(a, shard, lrow0, col0, reinterpret_cast<float*>(b0), wave, wm,
                                   wn, lane, acc, *src);
+  PK_MARK(a, 3);
 }
 
 // The persistent kernel: workgroup w takes walk positions w, w+G, w+2G, ...
@@ -1137,7 +1196,8 @@ __device__ __forceinline__ void reduce_units(const KArgs& a, int r, int nc, int 
 }
 
 template <class CS, class CO, int MODE, int GS, int ONE = 0>
-__global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
+__global__ void __launch_bounds__(CS::THREADS)
+    __attribute__((amdgpu_waves_per_eu(CS::OCC * CS::WAVES / 4))) pk_gemm_rs_fused(KArgs a) {
   using L = LdsPlan<CS, CO>;
   constexpr bool SPLIT = !__is_same(CS, CO);
   static_assert(CS::THREADS == CO::THREADS, "one workgroup size");
@@ -1149,6 +1209,7 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  PK_TL_START(a);
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous run of walk positions.
@@ -1207,6 +1268,7 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
     }
     fk = k + 1;
     npend = 0;
+    PK_MARK(a, 4);
   };
   if constexpr (MODE == kFusedReduce && SPLIT && GS == 7) {
     if (a.n_comm == 0) {
@@ -1304,7 +1366,49 @@ __global__ void __launch_bounds__(CS::THREADS) pk_gemm_rs_fused(KArgs a) {
       return;
     }
   }
-  if constexpr (ONE == 1) {
+  if constexpr (ONE == 2) {
+    static_assert(MODE == kFused && SPLIT && GS == 7 && CS::OCC == 2, "the two-per-CU schedule");
+    // Two workgroups share each CU (the host launches this instance only
+    // when the work fits): the first half of the grid, dispatched first, one
+    // per CU, and the second half beside it.  A first-half workgroup
+    // multiplies send tile j and sends it; the one beside it first takes
+    // owned sub-tile j (its peers read ahead into registers: mostly memory
+    // traffic, little MFMA), then multiplies send tile half + j and sends it.
+    // So while one workgroup of a CU multiplies, the other is reading peers
+    // or storing, and no workgroup waits for its own stores before its next
+    // loads.  Within each half the positions of one XCD are contiguous.
+    const int half = (int)(gridDim.x / 2);
+    const int b = blockIdx.x;
+    const bool first = b < half;
+    const int bb = first ? b : b - half;
+    const int j = (half & 7) == 0 ? (bb & 7) * (half >> 3) + (bb >> 3) : bb;
+    if (first) {
+      if (j < n_send) {
+        w = j;   // the walk position flush() signals
+        const TileCoord st = send_item(a.g, w);
+        process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
+                                            lds2, lds3, tid, wave, lane, nobg, nopv);
+        flush(0);
+      }
+    } else {
+      if (j < n_own) {
+        const TileCoord ot = owned_item(a.g, j);
+        const int sm = ot.sub / a.g.Rn, sn = ot.sub - sm * a.g.Rn;
+        process<CO, MODE, GS, kPeersPrefetch>(a, ot.shard, ot.t * CS::BM + sm * CO::BM,
+                                              ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
+                                              lds3, tid, wave, lane, nobg, nopv);
+      }
+      if (half + j < n_send) {
+        __syncthreads();   // the staging area is the send tile's first stage
+        w = half + j;
+        const TileCoord st = send_item(a.g, w);
+        process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
+                                            lds2, lds3, tid, wave, lane, nobg, nopv);
+        flush(0);
+      }
+    }
+    return;
+  } else if constexpr (ONE == 1) {
     static_assert(MODE == kFused && SPLIT && GS == 7, "the one-round schedule");
     {
       // The owned split in one round with workgroups to spare: G - n_send of
@@ -1452,6 +1556,7 @@ static const CfgInfo kCfgs[] = {
     {Cfg3::BM, Cfg3::BN, Cfg3::BK, Cfg3::WM, Cfg3::WN, Cfg3::THREADS},
     {Cfg4::BM, Cfg4::BN, Cfg4::BK, Cfg4::WM, Cfg4::WN, Cfg4::THREADS},
     {Cfg5::BM, Cfg5::BN, Cfg5::BK, Cfg5::WM, Cfg5::WN, Cfg5::THREADS},
+    {Cfg6::BM, Cfg6::BN, Cfg6::BK, Cfg6::WM, Cfg6::WN, Cfg6::THREADS},
 };
 static constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 static constexpr int kAssumedCUs = 256;   // MI355X; used only for the static pick
@@ -1510,6 +1615,7 @@ static int validate(const void* A, const void* B, const void* peers, const void*
   if (o && (o->store_policy < 0 || o->store_policy > 2)) return PK_ERR_CONFIG;
   if (o && o->ready_clock && (reinterpret_cast<uintptr_t>(o->ready_clock) & 7u))
     return PK_ERR_POINTER;
+  if (o && o->timeline && (reinterpret_cast<uintptr_t>(o->timeline) & 7u)) return PK_ERR_POINTER;
   if (M == 0 || N == 0) return PK_OK;     // nothing to write
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };
   if (!need(out)) return PK_ERR_POINTER;
@@ -1545,15 +1651,15 @@ static int validate_push(const void* A, const void* B, const void* accum, const 
 }
 
 // Resident workgroups per CU of one kernel instance, asked once per device.
-template <class CS, class CO, int MODE, int GS>
+template <class CS, class CO, int MODE, int GS, int ONE = 0>
 static int occupancy_of(int dev) {
   static int occ[64];
   static std::once_flag once[64];
   if (dev < 0 || dev >= 64) return 1;
   std::call_once(once[dev], [&] {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pk_gemm_rs_fused<CS, CO, MODE, GS>,
-                                                     CS::THREADS, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, pk_gemm_rs_fused<CS, CO, MODE, GS, ONE>, CS::THREADS, 0) != hipSuccess ||
         blocks < 1)
       blocks = 1;
     occ[dev] = blocks;
@@ -1588,6 +1694,7 @@ static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
   if (MODE == kFusedReduce && a.n_comm == 0 && grid < (long long)a.P * a.g.tiles_per_shard())
     return PK_ERR_CONFIG;
   if (grid > a.total_tiles) grid = a.total_tiles;
+  if (a.timeline && grid + a.n_comm > kTimelineWorkgroups) return PK_ERR_CONFIG;
   if constexpr (MODE == kFused && !__is_same(CS, CO) && GS == 7) {
     // the owned split in one round with workgroups to spare: its own schedule
     const long long n_send = split_sends(a.g), n_own = split_owned(a.g);
@@ -1599,6 +1706,25 @@ static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
   }
   hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CO, MODE, GS>), dim3((unsigned)(grid + a.n_comm)),
                      dim3(CS::THREADS), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
+}
+
+// The owned split in the two-per-CU schedule (configuration 6, P = 8): the
+// grid of two workgroups per CU; its first half holds a send tile each, its
+// second half every owned sub-tile and the remaining send tiles.  Returns
+// PK_ERR_CONFIG (nothing launched) when the work does not fit that grid.
+static int launch_two(KArgs& a, const pk_options* o, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_LAUNCH;
+  long long grid = (long long)cu_count(dev) * occupancy_of<Cfg6, CfgOwned3, kFused, 7, 2>(dev);
+  if (o && o->max_workgroups > 0 && o->max_workgroups < grid) grid = o->max_workgroups;
+  grid &= ~1LL;
+  const long long half = grid / 2;
+  const long long n_send = split_sends(a.g), n_own = split_owned(a.g);
+  if (half < 1 || n_own > half || n_send > grid) return PK_ERR_CONFIG;
+  if (a.timeline && grid > kTimelineWorkgroups) return PK_ERR_CONFIG;
+  hipLaunchKernelGGL((pk_gemm_rs_fused<Cfg6, CfgOwned3, kFused, 7, 2>), dim3((unsigned)grid),
+                     dim3(Cfg6::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
 }
 
@@ -1646,6 +1772,28 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
   a.g.Tn = ceil_div(a.N, C::BN);
   a.g.group_n = (o && o->group_n > 0) ? o->group_n : default_group_n(kCfgs[0], a.g.Tn);
   a.g.Rm = a.g.Rn = 1;
+  if constexpr (C::OCC == 2) {
+    // Two workgroups per CU: the plain GEMM and the staged share, the latter
+    // with the owned split in the two-per-CU schedule at P = 8 unless the
+    // split is turned off or the work does not fit it (then whole tiles).
+    if (mode != kGemmOnly && mode != kFused) return PK_ERR_CONFIG;
+    if (mode == kFused && a.P == 8 && !(o && o->owned_split < 0)) {
+      KArgs t = a;
+      t.g.Rm = C::BM / OwnedOf<C>::type::BM;
+      t.g.Rn = C::BN / OwnedOf<C>::type::BN;
+      t.total_tiles = split_pairs(t.g);
+      if (t.total_tiles == 0) return PK_OK;
+      if (2LL * (a.P - 1) * a.S * a.N < (1LL << 31) - 16) {
+        const int r = launch_two(t, o, stream);
+        if (r != PK_ERR_CONFIG) return r;
+      }
+    }
+    if (o && o->owned_split > 0) return PK_ERR_CONFIG;
+    a.total_tiles = a.g.total();
+    if (a.total_tiles == 0) return PK_OK;
+    if (gemm_only) return launch_as<C, C, kGemmOnly, 1>(a, o, stream);
+    return launch_staged<C, kFused>(a, false, o, stream);
+  } else {
   const bool split = staged_mode(mode) && use_owned_split(cfg, a.P, a.S, a.N, a.g.total(), o);
   if (split) {
     a.g.Rm = C::BM / CfgOwned::BM;
@@ -1663,6 +1811,7 @@ static int launch(KArgs& a, int mode, int cfg, const pk_options* o, hipStream_t 
   if (mode == kAgGemm) return launch_as<C, C, kAgGemm, 1>(a, o, stream);
   if (mode == kFusedReduce) return launch_staged<C, kFusedReduce>(a, split, o, stream);
   return launch_staged<C, kFused>(a, split, o, stream);
+  }
 }
 
 // Reduction role of the communicators (pk_gemm_rs_intercu_reduce).
@@ -1735,6 +1884,7 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
                    : (long long)a.S * N * (2LL * (a.P - 1) + (out_bf16 ? 2 : 4)));
   a.sig_batch = (o && o->signal_batch > 0) ? o->signal_batch : kDefaultSignalBatch;
   a.ready_clock = o ? o->ready_clock : nullptr;
+  a.timeline = o ? o->timeline : nullptr;
   a.wait_ready = nullptr;
   a.wait_expected = 0;
   a.spin_limit = 1;
@@ -1769,6 +1919,7 @@ static int run(const void* A, const void* B, const void* peers, void* send, void
     case 3: return launch<Cfg3>(a, mode, cfg, o, s);
     case 4: return launch<Cfg4>(a, mode, cfg, o, s);
     case 5: return launch<Cfg5>(a, mode, cfg, o, s);
+    case 6: return launch<Cfg6>(a, mode, cfg, o, s);
     default: return PK_ERR_CONFIG;
   }
 }
@@ -1795,6 +1946,7 @@ static int run_ag(const void* A, const uint32_t* a_ready, const void* B, void* C
                 error == nullptr || (reinterpret_cast<uintptr_t>(error) & 3u)))
     return PK_ERR_POINTER;
   KArgs a{};
+  a.timeline = o ? o->timeline : nullptr;
   a.A = static_cast<const uint16_t*>(A);
   a.B = static_cast<const uint16_t*>(B);
   a.out = Cout;
@@ -1826,6 +1978,7 @@ static int run_ag(const void* A, const uint32_t* a_ready, const void* B, void* C
     case 3: return launch<Cfg3>(a, kAgGemm, cfg, o, s);
     case 4: return launch<Cfg4>(a, kAgGemm, cfg, o, s);
     case 5: return launch<Cfg5>(a, kAgGemm, cfg, o, s);
+    case 6: return launch<Cfg6>(a, kAgGemm, cfg, o, s);
     default: return PK_ERR_CONFIG;
   }
 }
@@ -2066,7 +2219,7 @@ int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile
   if (tile_order < 0 || tile_order > 2) return PK_ERR_TILE_ORDER;
   if (M < 0 || N < 0 || M % P != 0) return PK_ERR_SHAPE;
   if (config < 1 || config > pk::kNumCfgs) return PK_ERR_CONFIG;
-  if (owned_split < 0 || (owned_split > 0 && config != 1)) return PK_ERR_CONFIG;
+  if (owned_split < 0 || (owned_split > 0 && config != 1 && config != 6)) return PK_ERR_CONFIG;
   const pk::CfgInfo& c = pk::kCfgs[config - 1];
   pk::Grid g;
   g.P = P;
@@ -2079,8 +2232,8 @@ int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile
   g.Tn = pk::ceil_div(N, c.BN);
   g.order = tile_order;
   g.group_n = group_n > 0 ? group_n : pk::default_group_n(c, g.Tn);
-  g.Rm = owned_split ? pk::Cfg1::BM / pk::CfgOwned::BM : 1;
-  g.Rn = owned_split ? pk::Cfg1::BN / pk::CfgOwned::BN : 1;
+  g.Rm = owned_split ? c.BM / pk::CfgOwned::BM : 1;
+  g.Rn = owned_split ? c.BN / pk::CfgOwned::BN : 1;
   const long long total = g.total();
   long long n = 0;
   auto put = [&](const pk::TileCoord& tc) {

@@ -103,7 +103,10 @@ typedef struct pk_options {
                            epilogue (P-1 peer reads per element) spreads over many
                            workgroups: 1 on, -1 off, 0 = auto (on when the walk has
                            fewer than two whole tiles per CU).  Tile configuration 1
-                           with P in {2, 4, 8} only; elsewhere it stays off. */
+                           with P in {2, 4, 8}, and configuration 6 (two workgroups
+                           per CU) at P = 8 when every owned sub-tile and send tile
+                           fits one grid of two workgroups per CU; elsewhere it
+                           stays off. */
   int signal_batch;     /* finished send tiles of a workgroup whose chunk arrivals
                            share one device-scope release, 0 = auto (8).  Larger
                            batches cost fewer cache writebacks and raise ready words
@@ -116,6 +119,13 @@ typedef struct pk_options {
                            1 streaming (non-temporal hint), 2 without the hint,
                            0 = auto (streaming when the call stores more than
                            64 MiB).  Results never depend on it. */
+  uint64_t* timeline;   /* NULL, or uint64 [2048][32] (8-byte aligned): read only by the
+                           instrumented timing build of this library
+                           (libpk_gemm_rs_timeline.so, compiled with PK_TIMELINE),
+                           which records per workgroup its CU placement and the
+                           device clock at each phase boundary; the launch must
+                           then have at most 2048 workgroups (else PK_ERR_CONFIG).
+                           Results never depend on it. */
 } pk_options;
 
 /* The fused share with explicit options; out_bf16 selects bf16 (1) or fp32 (0)
@@ -345,12 +355,14 @@ int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
  * min(cap, total) work items in the order they are handed out, (shard, row
  * tile, column tile, sub-tile) into out4[4*i .. 4*i+3]; sub-tile is -1 for a
  * whole tile and 0..R-1 for the R sub-tiles of an owned tile under the owned
- * split (owned_split = 1; only configuration 1), where the walk is a list of
+ * split (owned_split = 1; configurations 1 and 6), where the walk is a list of
  * pairs, each send tile followed by the owned sub-tile that rides with it.
  * When the split's pairs fit in one round of the grid at P = 8, the kernel
  * hands the sub-tiles of every fourth pair (pairs 0, 4, 8, ...) to the
  * workgroups that hold no send tile, and those pairs' workgroups only send;
- * the list is the same.  Returns the total number of work items or a
+ * the list is the same.  Configuration 6 hands send tile j to workgroup j of
+ * the first half of its grid and owned sub-tile j, then send tile half + j,
+ * to workgroup j of the second half.  Returns the total number of work items or a
  * negative code.  group_n as in
  * pk_options (0 = auto for this config). */
 int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,

@@ -57,13 +57,13 @@ MED = gen.Workload("medium", P=4, rank=1, M=1024, N=512, K=192, chunk_rows=64,
                    ab_dist="normal_sqrtk", peer_dist="normal", out_dtype="f32")
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("order", [0, 1, 2])
 def test_medium_integer_every_config_and_order(config, order):
     _run_and_check(MED, "f32", integer=True, order=order, config=config)
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_medium_real_every_config(config, out_dtype):
     _run_and_check(MED, out_dtype, integer=False, config=config)
@@ -75,7 +75,7 @@ RAGGED = gen.Workload("ragged", P=3, rank=2, M=600, N=328, K=136, chunk_rows=40,
                       ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("integer", [True, False])
 def test_ragged_tails(config, integer):
     _run_and_check(RAGGED, "bf16", integer=integer, config=config)
@@ -235,6 +235,30 @@ def test_outputs_invariant_across_orders_chunks_and_runs():
             H.expected_flags(CD, CD.chunk_rows, calls=n).view(np.int32)))
     assert torch.equal(share.send.view(torch.int16), ref[0])
     assert torch.equal(share.out.view(torch.int32), ref[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("order", [0, 1, 2])
+def test_two_per_cu_schedule(order):
+    """Configuration 6 at P = 8 runs the owned split with two workgroups per
+    CU (send tiles on the first half of the grid, owned sub-tiles then send
+    tiles on the second): bitwise the share of configuration 1, and the
+    oracle's on the integer twin."""
+    w = gen.WORKLOADS["comm_dominant"]
+    A, B, peers = gen.make_inputs(w, DEV, seed=81 + order)
+    ref = H.Share(w, "f32")
+    H.run(ref, A, B, peers, tile_order=order, config=1)
+    got = H.Share(w, "f32")
+    H.run(got, A, B, peers, tile_order=order, config=6)
+    torch.cuda.synchronize()
+    assert torch.equal(got.send.view(torch.int16), ref.send.view(torch.int16))
+    assert torch.equal(got.out.view(torch.int32), ref.out.view(torch.int32))
+    assert torch.equal(got.flags, ref.flags) and got.canaries_intact()
+    Ai, Bi, Pi = gen.make_inputs(w, DEV, seed=91 + order, integer=True)
+    sh = H.Share(w, "f32")
+    H.run(sh, Ai, Bi, Pi, tile_order=order, config=6)
+    torch.cuda.synchronize()
+    H.compare_exact(orc.gemm_rs_oracle(gen.bf16_bits(Ai), gen.bf16_bits(Bi), gen.bf16_bits(Pi),
+                                       w.P, w.rank, w.chunk_rows), sh)
 
 
 def test_bound_call_relaunches_the_same_share():
