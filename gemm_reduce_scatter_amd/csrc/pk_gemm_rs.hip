@@ -629,7 +629,16 @@ struct Seg {
 //                   a send tile just before this item (PresumStream);
 //  kPeersReduced  - summed by the communicator workgroups into presum (fp32),
 //                   read once its pieces' words have risen (reduce_units).
-enum PeerSource : int { kPeersDirect = 0, kPeersPrefetch = 1, kPeersPresum = 2, kPeersReduced = 3 };
+// kSendOnly marks a send tile under the owned split, which is never owned
+// (the owned shard is cut into sub-tiles of their own): its epilogue has no
+// owned branch.
+enum PeerSource : int {
+  kPeersDirect = 0,
+  kPeersPrefetch = 1,
+  kPeersPresum = 2,
+  kPeersReduced = 3,
+  kSendOnly = 4
+};
 
 __device__ __forceinline__ void add_bf16x8(float (&t)[8], u32x4 v) {
 #pragma unroll
@@ -780,7 +789,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
                         : C::OCC > 1        ? 1
                         : (C::FM * C::FN >= 4 ? 2 : (PASSES < 4 ? PASSES : 4));
   static_assert(PASSES % BATCH == 0, "batches tile the passes");
-  const bool owned = staged_mode(MODE) && shard == a.rank;
+  const bool owned = SRC != kSendOnly && staged_mode(MODE) && shard == a.rank;
   const int c8 = lane % LPR;
   const long long col = (long long)col0 + SG::col(wn, lane);
   const bool col_ok = col < a.N;
@@ -818,7 +827,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
             }
           }
         }
-      } else if (!owned) {
+      } else if (SRC == kSendOnly || !owned) {
 #pragma unroll
         for (int it = 0; it < PASSES; ++it) {
           const int rr = it * RPI + lane / LPR;
@@ -836,7 +845,7 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
             store16(dst, o, a.store_nt);
           }
         }
-      } else {
+      } else if constexpr (SRC != kSendOnly) {
 #pragma unroll
         for (int it0 = 0; it0 < PASSES; it0 += BATCH) {
           float t[BATCH][8];     // peer sums
@@ -886,11 +895,44 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
 #pragma unroll
           for (int b = 0; b < BATCH; ++b) {
             const int rr = (it0 + b) * RPI + lane / LPR;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
+            float* st8 = stage + rr * C::EPI_STRIDE + c8 * 8;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(st8);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(st8 + 4);
             float s8[8] = {t[b][0] + x0[0], t[b][1] + x0[1], t[b][2] + x0[2], t[b][3] + x0[3],
                            t[b][4] + x1[0], t[b][5] + x1[1], t[b][6] + x1[2], t[b][7] + x1[3]};
-            if (ok[b]) store_out(a, base[b], s8);
+            if (a.out_bf16) {
+              if (ok[b]) store_out(a, base[b], s8);
+            } else {
+              // fp32: the sums go back over the lane's staged values ...
+              *reinterpret_cast<f32x4*>(st8) = f32x4{s8[0], s8[1], s8[2], s8[3]};
+              *reinterpret_cast<f32x4*>(st8 + 4) = f32x4{s8[4], s8[5], s8[6], s8[7]};
+            }
+          }
+          if (!a.out_bf16) {
+            // ... and leave as two dense halves of each row's run of 8*LPR
+            // floats: lane c8 stores floats 4 c8 .. 4 c8 + 3, then 4 LPR +
+            // 4 c8 .., so every store instruction writes whole runs of 16 LPR
+            // bytes instead of every other 16 bytes (half-written lines would
+            // each be written through twice)
+            wave_lds_sync();
+            float* out32 = reinterpret_cast<float*>(a.out);
+            const long long colr = (long long)col0 + wn * C::WN;
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+              const int rr = (it0 + b) * RPI + lane / LPR;
+              const int lr = lrow0 + SG::row(wm, lane, fm, h, it0 + b);
+              const float* row = stage + rr * C::EPI_STRIDE;
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                const int c = half * 4 * LPR + 4 * c8;
+                const f32x4 y = *reinterpret_cast<const f32x4*>(row + c);
+                if (lr < a.S && colr + c < a.N)
+                  store16(out32 + (long long)lr * a.N + colr + c,
+                          u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                                __float_as_uint(y[3])},
+                          a.store_nt);
+              }
+            }
           }
         }
       }
@@ -1348,9 +1390,9 @@ __global__ void __launch_bounds__(CS::THREADS)
                                  1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (is_send) {
-        epilogue<CS, MODE, GS, kPeersDirect, NoPeers>(a, shard, lrow0, col0,
-                                                      reinterpret_cast<float*>(lds0), wave, wm,
-                                                      wn, lane, acc, nopv);
+        epilogue<CS, MODE, GS, kSendOnly, NoPeers>(a, shard, lrow0, col0,
+                                                   reinterpret_cast<float*>(lds0), wave, wm, wn,
+                                                   lane, acc, nopv);
         flush(0);
       } else if (wait_pieces(a, lrow0, col0, CS::BM, CS::BN, wave, lane)) {
         epilogue<CS, MODE, GS, kPeersReduced, NoPeers>(a, shard, lrow0, col0,
@@ -1386,7 +1428,7 @@ __global__ void __launch_bounds__(CS::THREADS)
       if (j < n_send) {
         w = j;   // the walk position flush() signals
         const TileCoord st = send_item(a.g, w);
-        process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
+        process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
                                             lds2, lds3, tid, wave, lane, nobg, nopv);
         flush(0);
       }
@@ -1402,7 +1444,7 @@ __global__ void __launch_bounds__(CS::THREADS)
         __syncthreads();   // the staging area is the send tile's first stage
         w = half + j;
         const TileCoord st = send_item(a.g, w);
-        process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
+        process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
                                             lds2, lds3, tid, wave, lane, nobg, nopv);
         flush(0);
       }
@@ -1435,7 +1477,7 @@ __global__ void __launch_bounds__(CS::THREADS)
       if (w < n_send) {
         const TileCoord st = send_item(a.g, w);
         if ((w & 3) == 0) {
-          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+          process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
           flush(0);
         } else {
@@ -1444,7 +1486,7 @@ __global__ void __launch_bounds__(CS::THREADS)
           const int olr = ot.t * CS::BM + sm * CO::BM, oc = ot.u * CS::BN + sn * CO::BN;
           PresumStream<CO, GS, CS::STAGES * CS::KK> ps;
           ps.init(a, olr, oc, wm, wn, lane);
-          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+          process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, ps, nopv);
           flush(0);
           __syncthreads();   // the staging area is the sub-tile's first stage
@@ -1478,7 +1520,7 @@ __global__ void __launch_bounds__(CS::THREADS)
       // the owned sub-tile's peer sum comes from the communicators
       if (s < n_send) {
         const TileCoord st = send_item(a.g, s);
-        process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+        process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                             lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
         if (++npend >= a.sig_batch || last) flush(k);
       }
@@ -1510,7 +1552,7 @@ __global__ void __launch_bounds__(CS::THREADS)
                                                 ot.u * CS::BN + sn * CO::BN, lds0, lds1, lds2,
                                                 lds3, tid, wave, lane, nobg, nopv);
           __syncthreads();   // the staging area is the send tile's first stage
-          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+          process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
           if (++npend >= a.sig_batch || last) flush(k);
         } else if (s < n_own) {
@@ -1519,14 +1561,14 @@ __global__ void __launch_bounds__(CS::THREADS)
           const int olr = ot.t * CS::BM + sm * CO::BM, oc = ot.u * CS::BN + sn * CO::BN;
           PresumStream<CO, GS, CS::STAGES * CS::KK> ps;
           ps.init(a, olr, oc, wm, wn, lane);
-          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+          process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, ps, nopv);
           if (++npend >= a.sig_batch || last) flush(k);
           __syncthreads();   // the staging area is the sub-tile's first stage
           process<CO, MODE, GS, kPeersPresum>(a, ot.shard, olr, oc, lds0, lds1, lds2, lds3, tid,
                                               wave, lane, nobg, ps);
         } else {
-          process<CS, MODE, GS, kPeersDirect>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
+          process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
                                               lds1, lds2, lds3, tid, wave, lane, nobg, nopv);
           if (++npend >= a.sig_batch || last) flush(k);
         }
