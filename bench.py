@@ -57,6 +57,10 @@ def parse():
                    help="also measure the K=2048 and K=8192 workloads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run 5 device copies of 512 MiB (counter calibration) and exit")
+    p.add_argument("--write-traffic", default=None, metavar="DIR",
+                   help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs found under DIR "
+                        "(<workload>_fetch, <workload>_write, copy_fetch, copy_write) into "
+                        "profiles/pmc_traffic.txt for the current kernel sources, and exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ag-gemm", action="store_true",
                    help="skip the all-gather + GEMM measurement (N x N/8 x N, N = 32768)")
@@ -500,6 +504,58 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": n, "calls": 5}), flush=True)
 
 
+TRAFFIC_CMD = ("rocprofv3 --pmc {counter} -f csv -d <DIR>/<workload>_{kind} -o p -- python3 "
+               "bench.py --workload <workload> --steps 5 --warmup 2 --no-secondary "
+               "--no-cpu-baseline --no-gemm-only --no-push --no-consumer --no-ag-gemm --no-reduce")
+COPY_CMD = "rocprofv3 --pmc {counter} -f csv -d <DIR>/copy_{kind} -o p -- python3 bench.py --copy-calibration"
+
+
+def write_traffic(d):
+    """profiles/pmc_traffic.txt from rocprofv3 counter runs under `d`: per
+    workload the median over the fused kernel's dispatches of FETCH_SIZE and
+    WRITE_SIZE (KiB), and the factors that make the counters read the bytes
+    of a plain 512 MiB device copy (one dispatch of the copy kernel moves
+    512 MiB each way)."""
+    import csv
+    import glob
+    import statistics
+
+    def per_dispatch(sub, counter, kernel_part):
+        files = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        vals = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and kernel_part in r["Kernel_Name"]:
+                    key = int(r["Dispatch_Id"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return sorted(vals.values())
+
+    copy_kib = 512 * 1024
+    cf = statistics.median(per_dispatch("copy_fetch", "FETCH_SIZE", "opy"))
+    cw = statistics.median(per_dispatch("copy_write", "WRITE_SIZE", "opy"))
+    rec = {"source_sha256": source_digest(),
+           "what": "fused kernel HBM traffic per launch: median over dispatches of rocprofv3 "
+                   "FETCH_SIZE / WRITE_SIZE (KiB), scaled by copy_*_factor = 524288 KiB / what "
+                   "the counter reads for one 512 MiB device copy",
+           "copy_fetch_factor": round(copy_kib / cf, 4), "copy_write_factor": round(copy_kib / cw, 4),
+           "commands": {"workload": TRAFFIC_CMD, "copy": COPY_CMD,
+                        "summary": "python bench.py --write-traffic <DIR>"},
+           "workloads": {}}
+    for sub in sorted(os.listdir(d)):
+        if not sub.endswith("_fetch") or sub.startswith("copy"):
+            continue
+        name = sub[:-len("_fetch")]
+        fe = per_dispatch(sub, "FETCH_SIZE", "pk_gemm_rs_fused")
+        wr = per_dispatch(name + "_write", "WRITE_SIZE", "pk_gemm_rs_fused")
+        if fe and wr:
+            rec["workloads"][name] = {"fetch_kib": round(statistics.median(fe), 1),
+                                      "write_kib": round(statistics.median(wr), 1),
+                                      "dispatches": [len(fe), len(wr)]}
+    with open(os.path.join(ROOT, "profiles", "pmc_traffic.txt"), "w") as f:
+        f.write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec), flush=True)
+
+
 def roofline_of(w, kernel_ms, metrics):
     if w.flops() / w.algorithmic_bytes() > metrics.PEAK_BF16_DENSE_FLOPS / metrics.PEAK_HBM_BYTES:
         ach = w.flops() / (kernel_ms * 1e-3) / 1e12
@@ -557,6 +613,9 @@ def main():
     from gemm_reduce_scatter_amd import inputs as gen
     from gemm_reduce_scatter_amd import metrics
 
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     torch.cuda.init()
     if args.copy_calibration:
         copy_calibration(torch)
