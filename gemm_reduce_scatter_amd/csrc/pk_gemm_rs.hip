@@ -1045,7 +1045,27 @@ struct LdsPlan {
 // owned item that takes its peer sum by prefetch (SRC kPeersPrefetch) reads
 // it into `pf`.  On return every stage load has landed and every wave has
 // passed a barrier, so the ring may be refilled.
-template <class C, int GS, int SRC, class BG, class PFT>
+// The first stages (0 .. S-2) of a work item into the ring b0, b1, ... as
+// main_part issues them; a caller that issues them early (before the previous
+// item's epilogue, so their latency hides behind its stores) then runs
+// main_part with PRE.
+template <class C>
+__device__ __forceinline__ void issue_prologue(const KArgs& a, int shard, int lrow0, int col0,
+                                               unsigned char* b0, unsigned char* b1,
+                                               unsigned char* b2, int wave, int lane) {
+  constexpr int S = C::STAGES, NQ = C::LOADS;
+  const long long row0 = (long long)shard * a.S + lrow0;
+  Loader<C> ld;
+  ld.init(a, wave, lane);
+  ld.bind(a, a.S - lrow0, col0);
+  if ((a.K + C::BK - 1) / C::BK > 0) {
+    ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), b0, wave);
+    if constexpr (S > 2) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
+    if constexpr (S > 3) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
+  }
+}
+
+template <class C, int GS, int SRC, class BG, class PFT, bool PRE = false>
 __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, int col0,
                                           unsigned char* b0, unsigned char* b1,
                                           unsigned char* b2, unsigned char* b3, int wave,
@@ -1068,16 +1088,17 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // prologue: stages 0 .. S-2
+  // prologue: stages 0 .. S-2 (already issued by the caller with PRE)
   constexpr int NQ = C::LOADS;
-  if (nk > 0) {
+  if (!PRE && nk > 0) {
     ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), b0, wave);
     if constexpr (S > 2) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
     if constexpr (S > 3) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
   }
   if (nk > 0) {
     // Loads complete in issue order, so this leaves stages 1 .. S-2 in
-    // flight; older stores of the previous item are retired too.
+    // flight; older stores of the previous item are retired too (with PRE,
+    // the stores issued after the prologue as well: the wait is only longer).
     wait_vm<(S - 2) * NQ>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -1115,7 +1136,7 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
 
 // One work item: its main loop (main_part), then its epilogue.  An owned
 // item takes its peer sum from source SRC (`pv` for kPeersPresum).
-template <class C, int MODE, int GS, int SRC, class BG, class PV>
+template <class C, int MODE, int GS, int SRC, class BG, class PV, bool PRE = false>
 __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, int col0,
                                         unsigned char* b0, unsigned char* b1, unsigned char* b2,
                                         unsigned char* b3, int tid, int wave, int lane, BG& bg,
@@ -1125,7 +1146,8 @@ __device__ __forceinline__ void process(const KArgs& a, int shard, int lrow0, in
   using PFT = typename std::conditional<SRC == kPeersPrefetch, PeerPrefetch<C, GS>, NoPeers>::type;
   PFT pf;
   f32x16 acc[C::FM][C::FN];
-  main_part<C, GS, SRC, BG, PFT>(a, shard, lrow0, col0, b0, b1, b2, b3, wave, lane, bg, pf, acc);
+  main_part<C, GS, SRC, BG, PFT, PRE>(a, shard, lrow0, col0, b0, b1, b2, b3, wave, lane, bg, pf,
+                                      acc);
   using PVT = typename std::conditional<SRC == kPeersPrefetch, PFT, PV>::type;
   const PVT* src;
   if constexpr (SRC == kPeersPrefetch) src = &pf;
@@ -1486,12 +1508,25 @@ __global__ void __launch_bounds__(CS::THREADS)
           const int olr = ot.t * CS::BM + sm * CO::BM, oc = ot.u * CS::BN + sn * CO::BN;
           PresumStream<CO, GS, CS::STAGES * CS::KK> ps;
           ps.init(a, olr, oc, wm, wn, lane);
-          process<CS, MODE, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0,
-                                              lds1, lds2, lds3, tid, wave, lane, ps, nopv);
+          {
+            f32x16 acc[CS::FM][CS::FN];
+            NoPeers nopf;
+            main_part<CS, GS, kSendOnly>(a, st.shard, st.t * CS::BM, st.u * CS::BN, lds0, lds1,
+                                         lds2, lds3, wave, lane, ps, nopf, acc);
+            // The sub-tile's first stages go into lds1 .. lds3 (its ring
+            // starts at lds1) while the send tile is re-laid in lds0 and
+            // stored, so their latency hides behind the stores; its ready
+            // words are raised after the sub-tile, with one wait and one
+            // release for both.
+            issue_prologue<CO>(a, ot.shard, olr, oc, lds1, lds2, lds3, wave, lane);
+            epilogue<CS, MODE, GS, kSendOnly, NoPeers>(a, st.shard, st.t * CS::BM, st.u * CS::BN,
+                                                       reinterpret_cast<float*>(lds0), wave, wm,
+                                                       wn, lane, acc, nopv);
+            PK_MARK(a, 3);
+          }
+          process<CO, MODE, GS, kPeersPresum, NoBackground, decltype(ps), true>(
+              a, ot.shard, olr, oc, lds1, lds2, lds3, lds0, tid, wave, lane, nobg, ps);
           flush(0);
-          __syncthreads();   // the staging area is the sub-tile's first stage
-          process<CO, MODE, GS, kPeersPresum>(a, ot.shard, olr, oc, lds0, lds1, lds2, lds3, tid,
-                                              wave, lane, nobg, ps);
         }
       } else {
         if (w < n_own) owned_ahead(w);
