@@ -8,9 +8,12 @@ number of calls made on it.  Prints ONE JSON line.
 
 Default workload: P = 8, rank 3, M = N = 4096, K = 512 (the HBM-bound,
 communication-dominant case), rotating buffer sets so the 256 MB
-last-level cache cannot serve the inputs.  The K = 4096 compute-bound case
-(M = N = 32768) is measured in the same run and reported under "secondary"
-(--secondary-all adds the K = 2048 and K = 8192 cases).
+last-level cache cannot serve the inputs.  The three M = N = 32768 shares
+(K = 2048, 4096 and 8192) are measured in the same run and reported under
+"secondary", each with at least 20 timed launches, its roofline and its own
+CPU-oracle baseline on a stated row block; the K = 8192 share is first swept
+over its 12 schedule points (chunk_rows x tile order) and reported at the
+best one.
 
 roofline.traffic is the fused kernel's measured HBM traffic per launch, read
 from profiles/pmc_traffic.txt (rocprofv3 FETCH_SIZE and WRITE_SIZE, each
@@ -53,8 +56,6 @@ def parse():
     p.add_argument("--owned-split", type=int, default=0, choices=(-1, 0, 1),
                    help="owned shard in 64x128 sub-tiles: 1 on, -1 off, 0 library default")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--secondary-all", action="store_true",
-                   help="also measure the K=2048 and K=8192 workloads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run 5 device copies of 512 MiB (counter calibration) and exit")
     p.add_argument("--write-traffic", default=None, metavar="DIR",
@@ -97,7 +98,7 @@ class BufferSet:
                    (self.A, self.B, self.peers, self.send, self.out))
 
 
-def time_steps(fn, n_sets, warmup, steps, torch, sample=None):
+def time_steps(fn, n_sets, warmup, steps, torch):
     """Run warmup + timed steps; returns (ms per step, wall seconds).
 
     A step is one launch of the kernel, issued through a pre-bound call so the
@@ -115,8 +116,6 @@ def time_steps(fn, n_sets, warmup, steps, torch, sample=None):
     for i in range(steps):
         fn((warmup + i) % n_sets)
     t_end.record()
-    if sample is not None:
-        sample()           # the host is ahead: the GPU is still running the steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return t_start.elapsed_time(t_end) / steps, wall
@@ -146,17 +145,7 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         launch[i]()
         calls[i] += 1
 
-    clocks = []
-
-    def sample():
-        for _ in range(20):
-            c = sclk_mhz()
-            if c is None:
-                return
-            clocks.append(c)
-            time.sleep(0.0005)
-
-    ms_step, wall = time_steps(step, n_sets, warmup, steps, torch, sample)
+    ms_step, wall = time_steps(step, n_sets, warmup, steps, torch)
     k_ms = ms_step
     # every ready word counts the calls on its set; every counter is back to 0
     for s, n in zip(sets, calls):
@@ -164,8 +153,7 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
         assert int(s.flags[:half].min()) == n and int(s.flags[:half].max()) == n
         assert int(s.flags[half:].abs().max()) == 0
     res = dict(ms_per_step=ms_step, kernel_ms=k_ms, wall_s=wall, n_sets=n_sets,
-               chunk_rows=chunk, tile_order=order,
-               sclk_mhz=(sorted(clocks)[len(clocks) // 2] if clocks else None))
+               chunk_rows=chunk, tile_order=order)
     if gemm_only:
         for s in sets:
             s.gemm_out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
@@ -305,22 +293,6 @@ def torch_mm_ms(w, torch, gen, steps=5, warmup=2):
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
     ms, _ = time_steps(lambda i: torch.mm(A, B, out=C), 1, warmup, steps, torch)
     return round(ms, 4)
-
-
-def sclk_mhz():
-    """Current shader clock of the first GPU from sysfs (the starred level of
-    pp_dpm_sclk), or None where the file is not readable."""
-    import glob
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            with open(path) as f:
-                for line in f:
-                    if line.strip().endswith("*"):
-                        return int(line.split(":")[1].strip().rstrip("*").strip().lower()
-                                   .replace("mhz", ""))
-        except (OSError, ValueError, IndexError):
-            continue
-    return None
 
 
 def measure_consumer(w, args, torch, gen, pk, reps=20, consumer_wgs=16):
@@ -568,21 +540,51 @@ def roofline_of(w, kernel_ms, metrics):
             "frac": round(ach / peak, 4), "traffic": traffic_for(w)}
 
 
-def cpu_baseline(w, gen, budget_s=12.0):
-    """The fp64 oracle on the host cores, on the full default share, repeated."""
-    import numpy as np  # noqa: F401
-    import oracle.gemm_rs_oracle as orc
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+        return int(max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()]))
     except Exception:
-        threads = os.cpu_count()
-    A, B, peers = gen.make_inputs(w, "cpu", seed=0)
-    Ab, Bb, Pb = gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers)
+        return int(os.cpu_count())
+
+
+def cpu_baseline(w, gen, torch, unit, rows_per_shard=None, budget_s=12.0):
+    """The fp64 oracle (oracle.gemm_rs_oracle as it is) on the host cores,
+    called repeatedly until ``budget_s`` has passed.
+
+    With ``rows_per_shard`` None it runs the whole share.  Otherwise it runs
+    the share restricted to the first ``rows_per_shard`` rows of each of the P
+    row shards: P * r rows of A, all of B, the same r rows of every peer slot,
+    chunks of r rows.  Every row does what it does in the whole share (N dot
+    products of length K, then its bf16 send rounding or its owned sum), so
+    the rate carries over to the whole share.  The inputs are the share's
+    generator output (made on the GPU); only the block goes to the host, and
+    neither that copy nor the bit extraction is timed.  ``value`` is in
+    ``unit``: GB/s of the block's algorithmic bytes or TFLOP/s of its
+    multiply-adds."""
+    import oracle.gemm_rs_oracle as orc
+    if rows_per_shard is None:
+        sub = w
+        A, B, peers = gen.make_inputs(w, "cpu", seed=0)
+        Ab, Bb, Pb = gen.bf16_bits(A), gen.bf16_bits(B), gen.bf16_bits(peers)
+        what = f"the whole {w.name} share ({w.M}x{w.N}x{w.K}, P={w.P})"
+    else:
+        r = rows_per_shard
+        sub = w.with_(M=w.P * r, chunk_rows=r)
+        dev = "cuda" if torch.cuda.is_available() else "cpu"
+        A, B, peers = gen.make_inputs(w, dev, seed=0)
+        rows = torch.cat([torch.arange(d * w.S, d * w.S + r) for d in range(w.P)]).to(A.device)
+        Ab, Bb, Pb = gen.bf16_bits(A[rows]), gen.bf16_bits(B), gen.bf16_bits(peers[:, :r])
+        what = (f"a row block of the {w.name} share ({w.M}x{w.N}x{w.K}, P={w.P}, rank {w.rank}): "
+                f"the first {r} rows of each of the {w.P} shards ({sub.M}x{w.N}x{w.K}, "
+                f"{w.P - 1} sent chunks and one owned sum of {r} rows each)")
+    del A, B, peers
+    if torch.cuda.is_available():
+        torch.cuda.empty_cache()
     n = 0
     t0 = time.perf_counter()
     while True:
-        orc.gemm_rs_oracle(Ab, Bb, Pb, w.P, w.rank, w.chunk_rows)
+        orc.gemm_rs_oracle(Ab, Bb, Pb, sub.P, sub.rank, sub.chunk_rows)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 50:
@@ -594,11 +596,62 @@ def cpu_baseline(w, gen, budget_s=12.0):
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(w.algorithmic_bytes() / per / 1e9, 3), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle", "cpu_model": model,
-            "sample": f"{n} full oracle calls of the {w.name} share ({w.M}x{w.N}x{w.K}, P={w.P}), "
-                      f"{per:.3f} s each, fp64 numpy/OpenBLAS",
-            "tflops_fp64": round(w.flops() / per / 1e12, 4)}
+    if unit == "TFLOP/s":
+        value = round(sub.flops() / per / 1e12, 4)
+    else:
+        value = round(sub.algorithmic_bytes() / per / 1e9, 3)
+    return {"value": value, "unit": unit, "cores": _blas_threads(), "kind": "oracle",
+            "cpu_model": model,
+            "sample": f"{n} oracle calls on {what}, {per:.3f} s each, fp64 numpy/OpenBLAS",
+            "tflops_fp64": round(sub.flops() / per / 1e12, 4),
+            "gbps": round(sub.algorithmic_bytes() / per / 1e9, 3)}
+
+
+def measure_secondary(w, args, torch, gen, pk, metrics, steps, warmup=3):
+    """One of the 32768-wide shares, timed like the default share (``steps``
+    back-to-back launches on one buffer set, which is larger than the
+    last-level cache).  A workload with sweep points (chunk_rows x tile order)
+    is first timed at every point; the best point is then timed again with
+    everything else, so the reported time is not the minimum of the sweep."""
+    a = argparse.Namespace(**{**vars(args), "chunk_rows": None, "tile_order": None})
+    chunk = order = None
+    sweep = None
+    if w.sweep_chunk_rows:
+        sweep = []
+        for c in w.sweep_chunk_rows:
+            for o in (0, 1, 2):
+                r = measure(w, a, torch, gen, pk, metrics, steps, warmup, rotate=False,
+                            gemm_only=False, tile_order=o, chunk_rows=c)
+                sweep.append({"chunk_rows": c, "tile_order": o,
+                              "kernel_ms": round(r["kernel_ms"], 4)})
+        best = min(sweep, key=lambda p: p["kernel_ms"])
+        chunk, order = best["chunk_rows"], best["tile_order"]
+    r = measure(w, a, torch, gen, pk, metrics, steps, warmup, rotate=False,
+                gemm_only=not args.no_gemm_only, tile_order=order, chunk_rows=chunk,
+                reduce_counts=() if args.no_reduce else (16, 32),
+                # owned tiles wait for the reduction: an order that reaches
+                # them late (row-major; the owned shard is rank's)
+                reduce_order=0)
+    roof = roofline_of(w, r["kernel_ms"], metrics)
+    sec = {"workload": w.name, "P": w.P, "rank": w.rank, "M": w.M, "N": w.N, "K": w.K,
+           "out": w.out_dtype, "chunk_rows": r["chunk_rows"], "tile_order": r["tile_order"],
+           "steps": steps, "warmup": warmup, "kernel_ms": round(r["kernel_ms"], 4),
+           "tflops": round(w.flops() / (r["kernel_ms"] * 1e-3) / 1e12, 2), "roofline": roof}
+    if sweep is not None:
+        sec["sweep"] = sweep
+    if "gemm_only_kernel_ms" in r:
+        sec["gemm_only_kernel_ms"] = round(r["gemm_only_kernel_ms"], 4)
+        sec["exposed_fraction"] = round(r["exposed_fraction"], 4)
+    if "inter_cu_reduce" in r:
+        sec["inter_cu_reduce"] = r["inter_cu_reduce"]
+    if not args.no_push:
+        pu = measure_push(w, args, torch, gen, pk, steps, warmup)
+        sec["atomic_push_kernel_ms"] = pu["kernel_ms"]
+    sec["torch_mm_ms"] = torch_mm_ms(w, torch, gen, steps=steps, warmup=warmup)
+    if not args.no_cpu_baseline:
+        sec["cpu_baseline"] = cpu_baseline(w, gen, torch, roof["unit"], rows_per_shard=64,
+                                           budget_s=6.0)
+    return sec
 
 
 def main():
@@ -670,43 +723,16 @@ def main():
         line["gemm_only_kernel_ms"] = round(r["gemm_only_kernel_ms"], 5)
         line["exposed_fraction"] = round(r["exposed_fraction"], 4)
         line["torch_mm_ms"] = torch_mm_ms(w, torch, gen, steps=max(5, min(args.steps, 50)))
-    line["sclk_mhz_during"] = r["sclk_mhz"]
     if "inter_cu_reduce" in r:
         line["inter_cu_reduce"] = r["inter_cu_reduce"]
     if not args.no_secondary:
-        names = ["compute_bound"]
-        if args.secondary_all:
-            names = ["near_threshold", "compute_bound", "large_k"]
-        secs = []
-        for name in names:
-            if name == args.workload:
-                continue
-            w2 = gen.WORKLOADS[name]
-            r2 = measure(w2, args.__class__(**{**vars(args), "chunk_rows": None,
-                                               "tile_order": None}), torch, gen, pk,
-                         metrics, min(20, max(5, args.steps // 5)), 3, rotate=False,
-                         gemm_only=not args.no_gemm_only,
-                         reduce_counts=() if args.no_reduce else (16, 32),
-                         # owned tiles wait for the reduction: an order that reaches
-                         # them late (row-major; the owned shard is rank's)
-                         reduce_order=0)
-            sec = {"workload": w2.name, "K": w2.K, "M": w2.M, "tile_order": r2["tile_order"],
-                   "sclk_mhz_during": r2["sclk_mhz"],
-                   "chunk_rows": r2["chunk_rows"], "kernel_ms": round(r2["kernel_ms"], 4),
-                   "tflops": round(w2.flops() / (r2["kernel_ms"] * 1e-3) / 1e12, 2),
-                   "roofline": roofline_of(w2, r2["kernel_ms"], metrics)}
-            if "gemm_only_kernel_ms" in r2:
-                sec["gemm_only_kernel_ms"] = round(r2["gemm_only_kernel_ms"], 4)
-                sec["exposed_fraction"] = round(r2["exposed_fraction"], 4)
-            if "inter_cu_reduce" in r2:
-                sec["inter_cu_reduce"] = r2["inter_cu_reduce"]
-            if not args.no_push:
-                pu = measure_push(w2, args, torch, gen, pk, min(20, max(5, args.steps // 5)), 3)
-                sec["atomic_push_kernel_ms"] = pu["kernel_ms"]
-            sec["torch_mm_ms"] = torch_mm_ms(w2, torch, gen)
-            secs.append(sec)
+        # at least 20 timed launches each (a compute-bound launch is 4-14 ms)
+        sec_steps = max(20, args.steps // 10)
+        secs = [measure_secondary(gen.WORKLOADS[name], args, torch, gen, pk, metrics, sec_steps)
+                for name in ("near_threshold", "compute_bound", "large_k")
+                if name != args.workload]
         if secs:
-            line["secondary"] = secs[0] if len(secs) == 1 else secs
+            line["secondary"] = secs
     if not args.no_push:
         pu = measure_push(w, args, torch, gen, pk, args.steps, args.warmup)
         pu["vs_staged"] = round(pu["kernel_ms"] / r["kernel_ms"], 3)
@@ -718,7 +744,7 @@ def main():
     if not args.no_ag_gemm:
         line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, min(20, max(5, args.steps // 5)), 3)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, gen)
+        line["cpu_baseline"] = cpu_baseline(w, gen, torch, unit)
     print(json.dumps(line), flush=True)
 
 
