@@ -1049,11 +1049,21 @@ struct LdsPlan {
 // main_part issues them; a caller that issues them early (before the previous
 // item's epilogue, so their latency hides behind its stores) then runs
 // main_part with PRE.
+// An item's coordinates are the same in every lane, but the compiler cannot
+// always prove it (an item chosen after a wait whose result went through LDS,
+// say); read from the first lane they stay in scalar registers, and so do
+// the buffer descriptors built from them (a descriptor taken for divergent
+// costs a loop over the lanes around every load that uses it).
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <class C>
 __device__ __forceinline__ void issue_prologue(const KArgs& a, int shard, int lrow0, int col0,
                                                unsigned char* b0, unsigned char* b1,
                                                unsigned char* b2, int wave, int lane) {
   constexpr int S = C::STAGES, NQ = C::LOADS;
+  shard = uniform_int(shard);
+  lrow0 = uniform_int(lrow0);
+  col0 = uniform_int(col0);
   const long long row0 = (long long)shard * a.S + lrow0;
   Loader<C> ld;
   ld.init(a, wave, lane);
@@ -1073,6 +1083,9 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
                                           f32x16 (&acc)[C::FM][C::FN]) {
   constexpr int S = C::STAGES;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  shard = uniform_int(shard);
+  lrow0 = uniform_int(lrow0);
+  col0 = uniform_int(col0);
   const long long row0 = (long long)shard * a.S + lrow0;
   Loader<C> ld;
   ld.init(a, wave, lane);
