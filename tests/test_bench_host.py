@@ -58,3 +58,38 @@ def test_source_digest_covers_every_kernel_source():
     names = sorted(os.listdir(d))
     assert any(n.endswith(".hip") for n in names)
     assert len(bench.source_digest()) == 64
+
+
+def test_cpu_baseline_row_block_is_the_share_restricted_to_those_rows(monkeypatch):
+    """The oracle, unchanged, runs on the first r rows of each of the P shards:
+    P*r rows of A, all of B, the same r rows of every peer slot, chunks of r
+    rows; the rate is reported for that block's work."""
+    import numpy as np
+    import torch
+    import oracle.gemm_rs_oracle as orc
+    w = gen.Workload("small", P=4, rank=1, M=512, N=256, K=64, chunk_rows=32,
+                     ab_dist="normal_sqrtk", peer_dist="normal", out_dtype="bf16")
+    r = 16
+    seen = {}
+    real = orc.gemm_rs_oracle
+    clock = [0.0]    # each oracle call takes exactly 1 us on this clock
+
+    def spy(A_bits, B_bits, peer_bits, P, rank, chunk_rows):
+        seen.update(A=A_bits, B=B_bits, peers=peer_bits, P=P, rank=rank, chunk=chunk_rows)
+        clock[0] += 1e-6
+        return real(A_bits, B_bits, peer_bits, P, rank, chunk_rows)
+
+    monkeypatch.setattr(orc, "gemm_rs_oracle", spy)
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: clock[0])
+    cb = bench.cpu_baseline(w, gen, torch, "TFLOP/s", rows_per_shard=r, budget_s=0.0)
+    A, B, peers = gen.make_inputs(w, "cpu", seed=0)
+    rows = np.concatenate([np.arange(d * w.S, d * w.S + r) for d in range(w.P)])
+    assert np.array_equal(seen["A"], gen.bf16_bits(A)[rows])
+    assert np.array_equal(seen["B"], gen.bf16_bits(B))
+    assert np.array_equal(seen["peers"], gen.bf16_bits(peers)[:, :r])
+    assert (seen["P"], seen["rank"], seen["chunk"]) == (w.P, w.rank, r)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["cores"] >= 1
+    assert f"the first {r} rows of each of the {w.P} shards" in cb["sample"]
+    sub = w.with_(M=w.P * r, chunk_rows=r)
+    assert cb["value"] == pytest.approx(sub.flops() / 1e-6 / 1e12, abs=1e-4)
+    assert cb["gbps"] == pytest.approx(sub.algorithmic_bytes() / 1e-6 / 1e9, abs=1e-3)
