@@ -1537,9 +1537,21 @@ __global__ void __launch_bounds__(CS::THREADS)
                                                        wn, lane, acc, nopv);
             PK_MARK(a, 3);
           }
-          process<CO, MODE, GS, kPeersPresum, NoBackground, decltype(ps), true>(
-              a, ot.shard, olr, oc, lds1, lds2, lds3, lds0, tid, wave, lane, nobg, ps);
-          flush(0);
+          // The send tile's stores were issued before the sub-tile's main
+          // loop: release them and raise its ready words once that loop is
+          // done, so the release does not also wait for the sub-tile's own
+          // stores (which need none); wave 0 releases while the others start
+          // the sub-tile's epilogue.
+          {
+            f32x16 acc[CO::FM][CO::FN];
+            NoPeers nopf;
+            main_part<CO, GS, kPeersPresum, NoBackground, NoPeers, true>(
+                a, ot.shard, olr, oc, lds1, lds2, lds3, lds0, wave, lane, nobg, nopf, acc);
+            flush(0);
+            epilogue<CO, MODE, GS, kPeersPresum, decltype(ps)>(
+                a, ot.shard, olr, oc, reinterpret_cast<float*>(lds1), wave, wm, wn, lane, acc, ps);
+            PK_MARK(a, 3);
+          }
         }
       } else {
         if (w < n_own) owned_ahead(w);
