@@ -482,10 +482,11 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
       // this and the previous step), so the barrier also ends all use of it.
       // Loads complete in issue order; younger than the next stage's are
       // the stages after it issued so far (all but this step's share of the
-      // newest one when it comes late) and the background loads of the last
-      // two stages, which may stay in flight.
+      // newest one when it comes late) and the background loads issued
+      // since its last share: those of the last STAGES - 2 stages, which may
+      // stay in flight.
       wait_vm<(C::STAGES - 2) * C::LOADS - (LATE ? Q1 - Q0 : 0) +
-              2 * C::KK * BG::LOADS_PER_STEP>();
+              (C::STAGES - 2) * C::KK * BG::LOADS_PER_STEP>();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
