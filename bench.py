@@ -742,7 +742,7 @@ def main():
     if not args.no_consumer and w.P > 1:
         line["inter_cu"] = measure_intercu(w, args, torch, gen, pk, args.steps, args.warmup)
     if not args.no_ag_gemm:
-        line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, min(20, max(5, args.steps // 5)), 3)
+        line["ag_gemm"] = measure_ag_gemm(torch, gen, pk, max(20, args.steps // 10), 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gen, torch, unit)
     print(json.dumps(line), flush=True)
