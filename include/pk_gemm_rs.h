@@ -95,7 +95,8 @@ int pk_gemm_rs_local_bf16out(const void* A, const void* B, const void* peer_part
 typedef struct pk_options {
   int config;           /* tile configuration id (pk_config_info), 0 = auto */
   int max_workgroups;   /* cap on the persistent grid, 0 = fill the device */
-  int group_n;          /* column tiles per locality group inside a shard, 0 = auto */
+  int group_n;          /* column tiles per locality group inside a shard; 0 = auto: 32 for
+                           dest-round-robin, 8 for the other orders (at most the tile columns) */
   int gemm_only;        /* 1: store bf16(A*B) for all M rows into `out` (bf16 [M][N]);
                            no send, peers or flags.  The standalone-GEMM reference
                            the fused kernel is measured against. */

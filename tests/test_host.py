@@ -227,8 +227,9 @@ def test_owned_split_walk_pairs_send_tiles_with_owned_sub_tiles():
             assert list(sends[::per, 0]) == [(rank + 1 + k) % P for k in range(P - 1)]
         else:
             assert np.array_equal(sends[:, :3], ref[:, :3])
-        # owned sub-tiles: owned tile j // R, sub-tile j % R, in the owned shard's order
-        own_ref = whole[0][whole[0][:, 0] == rank]
+        # owned sub-tiles: owned tile j // R, sub-tile j % R, in the owned shard's
+        # order under this tile order (its column groups may differ by order)
+        own_ref = whole[order][whole[order][:, 0] == rank]
         assert list(owned[:, 3]) == [j % OWNED_R for j in range(OWNED_R * per)]
         assert np.array_equal(owned[:, 1:3], np.repeat(own_ref[:, 1:3], OWNED_R, axis=0))
         # pairing: item 2s is send tile s, item 2s+1 its owned sub-tile
