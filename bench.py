@@ -121,6 +121,12 @@ def time_steps(fn, n_sets, warmup, steps, torch):
     return t_start.elapsed_time(t_end) / steps, wall
 
 
+def ready_words(w, chunk_rows):
+    """Ready words at the front of the flags buffer, one per chunk of each
+    send slot; the counters after them are zero between calls."""
+    return (w.P - 1) * (w.S // chunk_rows) if w.S > 0 else 0
+
+
 def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_only=True,
             tile_order=None, chunk_rows=None, reduce_counts=(), reduce_order=None):
     chunk = chunk_rows or args.chunk_rows or w.chunk_rows
@@ -148,10 +154,10 @@ def measure(w, args, torch, gen, pk, metrics, steps, warmup, rotate=True, gemm_o
     ms_step, wall = time_steps(step, n_sets, warmup, steps, torch)
     k_ms = ms_step
     # every ready word counts the calls on its set; every counter is back to 0
+    nr = ready_words(w, chunk)
     for s, n in zip(sets, calls):
-        half = s.flags.numel() // 2
-        assert int(s.flags[:half].min()) == n and int(s.flags[:half].max()) == n
-        assert int(s.flags[half:].abs().max()) == 0
+        assert int(s.flags[:nr].min()) == n and int(s.flags[:nr].max()) == n
+        assert int(s.flags[nr:].abs().max()) == 0
     res = dict(ms_per_step=ms_step, kernel_ms=k_ms, wall_s=wall, n_sets=n_sets,
                chunk_rows=chunk, tile_order=order)
     if gemm_only:
@@ -205,9 +211,9 @@ def measure_reduce(w, sets, calls, chunk, order, out_bf16, opts, counts, steps, 
         for call in launch:
             assert call.check() == 0, "a reduction wait gave up"
         res[str(nc)] = round(ms * 1e3, 2) if ms < 1 else round(ms, 4)
+    nw = ready_words(w, chunk)
     for s, (ps, pw, er), n, nr in zip(sets, side, calls, red_calls):
-        half = s.flags.numel() // 2
-        assert int(s.flags[:half].min()) == n and int(s.flags[half:].abs().max()) == 0
+        assert int(s.flags[:nw].min()) == n and int(s.flags[nw:].abs().max()) == 0
         assert int(pw.min()) == nr and int(pw.max()) == nr and int(er.item()) == 0
     best = min(res, key=res.get)
     unit = "us_per_call_by_comm_cus" if fused_ms < 1 else "ms_per_call_by_comm_cus"

@@ -107,6 +107,11 @@ def _open(path: str):
     lib.pk_tile_walk.restype = i64
     lib.pk_chunk_arrivals.argtypes = [i64, i64, i32, i32, i32, i32]
     lib.pk_chunk_arrivals.restype = i64
+    lib.pk_gather_rows.argtypes = [i32, i32, i64, i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.pk_gather_rows.restype = i32
+    lib.pk_gather_arrivals.argtypes = [i64, i64, i32, i32, ctypes.POINTER(ctypes.c_uint32),
+                                       ctypes.POINTER(ctypes.c_uint32)]
+    lib.pk_gather_arrivals.restype = i32
     lib.pk_strerror.argtypes = [i32]
     lib.pk_strerror.restype = ctypes.c_char_p
     lib.pk_version.argtypes = []
@@ -721,6 +726,29 @@ def pk_tile_walk(M, N, P, rank, config, tile_order, group_n=0, owned_split=0) ->
 def pk_chunk_arrivals(M, N, P, chunk_rows, config, c) -> int:
     return _check(load().pk_chunk_arrivals(int(M), int(N), int(P), int(chunk_rows),
                                            int(config), int(c)))
+
+
+def pk_gather_rows(P, rank, M, g) -> np.ndarray:
+    """Rows of A that tile rows 0..255 of row group g read under the
+    gathered-row schedule (int64 [256])."""
+    rows = np.zeros(256, dtype=np.int64)
+    _check(load().pk_gather_rows(int(P), int(rank), int(M), int(g),
+                                 rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return rows
+
+
+def pk_gather_arrivals(M, N, P, chunk_rows):
+    """(expected, made): arrivals each chunk of each send slot waits for under
+    the gathered-row schedule and the arrivals its work items make, both
+    uint32 [P-1][S/chunk_rows]."""
+    n = (P - 1) * (M // P // chunk_rows) if P > 1 and chunk_rows > 0 else 0
+    exp = np.zeros(max(n, 1), dtype=np.uint32)
+    made = np.zeros(max(n, 1), dtype=np.uint32)
+    _check(load().pk_gather_arrivals(int(M), int(N), int(P), int(chunk_rows),
+                                     exp.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                     made.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))))
+    shape = (P - 1, M // P // chunk_rows)
+    return exp[:n].reshape(shape), made[:n].reshape(shape)
 
 
 def pk_version() -> int:

@@ -322,6 +322,17 @@ struct Loader {
     b_vo = col0 + b_nc < a.N ? b_off : kOffNone;
   }
 
+  // Gathered rows: the A row of load q is tile row a_row + q*WAVES*A_RPL of
+  // row group g, at its own row of A (gather_row); the stage descriptor then
+  // starts at row 0 and the loads take no row step.
+  __device__ __forceinline__ void bind_gather(const KArgs& a, int g, int col0) {
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q)
+      a_vo[q] = (uint32_t)(gather_row(a.rank, a.S, g, a_row + q * C::WAVES * C::A_RPL) * a.K +
+                           a_kc) * 2u;
+    b_vo = col0 + b_nc < a.N ? b_off : kOffNone;
+  }
+
   // Per-stage descriptors: A rows from row0, B columns from col0, both at k0.
   struct Stage {
     __amdgpu_buffer_rsrc_t ra, rb;
@@ -347,14 +358,14 @@ struct Loader {
   // K through the stage descriptor's range, and A's k-columns past K
   // (which the range of a row-strided A cannot cut off) through one compare
   // per call, shared by all A loads of the lane.
-  template <int Q0, int Q1>
+  template <int Q0, int Q1, bool GA = false>
   __device__ __forceinline__ void issue(const KArgs& a, const Stage& st,
                                         unsigned char* dst, int wave) const {
     const bool a_k_ok = st.k0 + a_kc < a.K;
 #pragma unroll
     for (int q = Q0; q < Q1; ++q) {
       if (q < C::A_LOADS) {
-        const uint32_t soff = (uint32_t)(q * C::WAVES * C::A_RPL) * (uint32_t)a.K * 2u;
+        const uint32_t soff = GA ? 0u : (uint32_t)(q * C::WAVES * C::A_RPL) * (uint32_t)a.K * 2u;
         dma16(st.ra, (PK_LDS void*)(dst + (q * C::WAVES + wave) * 1024),
               a_k_ok ? a_vo[q] : kOffNone, soff);
       } else {
@@ -459,7 +470,7 @@ __device__ __forceinline__ void step_pattern() {
 // loads in flight is fixed, and the accumulators stay in place across
 // iterations.  `bg` gets one hook per step (step STG*KK + kk of the trip) to
 // issue background loads; it issues BG::LOADS_PER_STEP of them.
-template <class C, int STG, int KKI, class BG>
+template <class C, int STG, int KKI, class BG, bool GA = false>
 __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
                                             const typename Loader<C>::Stage& ns,
                                             const Reader<C>& rd, const unsigned char* cur,
@@ -473,7 +484,7 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
     // With three or more stages the last step's loads wait until after the
     // barrier, so every step spreads its loads over its MFMAs.
     constexpr bool LATE = KKI + 1 == C::KK && C::STAGES >= 3;
-    if constexpr (!LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave);
+    if constexpr (!LATE) ld.template issue<Q0, Q1, GA>(a, ns, nxt, wave);
     bg.template step<STG * C::KK + KKI>(a);
     if constexpr (KKI + 1 < C::KK) {
       rd.read(cur, KKI + 1, f[(KKI + 1) & 1]);
@@ -492,17 +503,17 @@ __device__ __forceinline__ void stage_steps(const KArgs& a, const Loader<C>& ld,
       asm volatile("" ::: "memory");
       // `nxt` was last read in the stage before this one, before the
       // previous barrier.
-      if constexpr (LATE) ld.template issue<Q0, Q1>(a, ns, nxt, wave);
+      if constexpr (LATE) ld.template issue<Q0, Q1, GA>(a, ns, nxt, wave);
       rd.read(nbuf, 0, f[(KKI + 1) & 1]);
     }
     Reader<C>::mfma(f[KKI & 1], acc);
     step_pattern<0, C::FM * C::FN, C::FM + 2 * C::FN, (KKI + 1 < C::KK || LATE) ? Q1 - Q0 : 0>();
     __builtin_amdgcn_sched_barrier(0);
-    stage_steps<C, STG, KKI + 1, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, acc, f, bg);
+    stage_steps<C, STG, KKI + 1, BG, GA>(a, ld, ns, rd, cur, nxt, nbuf, wave, acc, f, bg);
   }
 }
 
-template <class C, int STG, class BG>
+template <class C, int STG, class BG, bool GA = false>
 __device__ __forceinline__ void main_stage(const KArgs& a, const Loader<C>& ld,
                                            const typename Loader<C>::Stage& ns,
                                            const Reader<C>& rd, const unsigned char* cur,
@@ -510,7 +521,7 @@ __device__ __forceinline__ void main_stage(const KArgs& a, const Loader<C>& ld,
                                            int wave, f32x16 (&acc)[C::FM][C::FN],
                                            typename Reader<C>::Frags (&f)[2], BG& bg) {
   static_assert(C::KK % 2 == 0, "the next stage's first fragments land in f[0]");
-  stage_steps<C, STG, 0, BG>(a, ld, ns, rd, cur, nxt, nbuf, wave, acc, f, bg);
+  stage_steps<C, STG, 0, BG, GA>(a, ld, ns, rd, cur, nxt, nbuf, wave, acc, f, bg);
 }
 
 // No background work.
@@ -543,15 +554,20 @@ __device__ __forceinline__ unsigned char* pick(unsigned char* b0, unsigned char*
 // counter and their wait waits for it to reach a value: call n of a flags
 // buffer raises its ready words to n, and nothing has to clear them between
 // calls) and resets the counter for the next launch.
+// Each chunk's arrival counter has a 128-byte line of its own (counter idx
+// at word kCounterStride * idx of the counter area): the arrivals of one
+// launch at different chunks then do not queue behind each other at one line
+// (measured 2-3 us of the comm-dominant share with all counters in one line).
+constexpr int kCounterStride = 32;
 __device__ __forceinline__ void signal_chunk(const KArgs& a, int idx, uint32_t want) {
   uint32_t* ready = a.flags;
-  uint32_t* counters = a.flags + (long long)(a.P - 1) * a.n_chunks;
-  const uint32_t old = __hip_atomic_fetch_add(&counters[idx], 1u, __ATOMIC_RELAXED,
+  uint32_t* counter = a.flags + (long long)(a.P - 1) * a.n_chunks + (long long)kCounterStride * idx;
+  const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
   if (old + 1u == want) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __hip_atomic_fetch_add(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&counters[idx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.ready_clock) a.ready_clock[idx] = wall_clock64();
   }
 }
@@ -684,21 +700,20 @@ struct PeerPrefetch {
   }
 };
 
-// The peer sum of an owned sub-tile (configuration CO, GS = P-1 slots),
-// accumulated by a workgroup while it multiplies a send tile whose main loop
-// has STEPS k16 steps per trip.  Load g (g = trip*STEPS + step) reads slot
-// g/SEGS of segment g%SEGS; each segment keeps two loads in flight and adds
-// one when it issues the load two slots later, 2*SEGS steps after it was
-// issued, so a load has that many steps of MFMA to land in.  The loads go through a
-// buffer descriptor over the peer partials: slots past P-2 get an offset
-// past its range and read zeros, which add nothing (the sums start at +0
-// and never hold -0).  finish() adds the last loads and any slots a short K
-// left unread.  Byte offsets are 32-bit: the owned split requires the peer
+// The peer sums of SEGS segments of 8 owned elements per lane (GS = P-1
+// slots), accumulated by a workgroup while it multiplies a tile whose main
+// loop has STEPS k16 steps per trip.  Load g (g = trip*STEPS + step) reads
+// slot g/SEGS of segment g%SEGS; each segment keeps two loads in flight and
+// adds one when it issues the load two slots later, 2*SEGS steps after it
+// was issued, so a load has that many steps of MFMA to land in.  The loads go
+// through a buffer descriptor over the peer partials: slots past P-2 get an
+// offset past its range and read zeros, which add nothing (the sums start at
+// +0 and never hold -0).  finish() adds the last loads and any slots a short
+// K left unread.  Byte offsets are 32-bit: the owned split requires the peer
 // partials to span less than 2^31 bytes.
-template <class CO, int GS, int STEPS>
-struct PresumStream {
-  using SG = Seg<CO>;
-  static constexpr int SEGS = SG::COUNT;
+template <int SEGS_, int GS, int STEPS>
+struct PeerStream {
+  static constexpr int SEGS = SEGS_;
   static constexpr int SPT = STEPS / SEGS;              // slots per trip
   static constexpr int LOADS_PER_STEP = 1;
   static_assert(STEPS % SEGS == 0, "whole segments per trip");
@@ -709,22 +724,15 @@ struct PresumStream {
   __amdgpu_buffer_rsrc_t rsrc;
   int trip;
 
-  __device__ __forceinline__ void init(const KArgs& a, int lrow0, int col0, int wm, int wn,
-                                       int lane) {
+  // Segment sg at shard-local row lr, column col (outside the shard: row 0,
+  // whose sums are never stored).
+  __device__ __forceinline__ void set(const KArgs& a, int sg, int lr, int col) {
+    const bool ok = lr < a.S && col < a.N;
+    off[sg] = ok ? ((uint32_t)lr * (uint32_t)a.N + (uint32_t)col) * 2u : 0u;
+  }
+  __device__ __forceinline__ void start(const KArgs& a) {
     rsrc = make_rsrc(a.peers);
     slot_bytes = (uint32_t)a.S * (uint32_t)a.N * 2u;
-    const int col = col0 + SG::col(wn, lane);
-#pragma unroll
-    for (int fm = 0; fm < CO::FM; ++fm)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int it = 0; it < SG::PASSES; ++it) {
-          const int lr = lrow0 + SG::row(wm, lane, fm, h, it);
-          const bool ok = lr < a.S && col < a.N;
-          const int sg = (fm * 2 + h) * SG::PASSES + it;
-          off[sg] = ok ? ((uint32_t)lr * (uint32_t)a.N + (uint32_t)col) * 2u : 0u;   // row 0 stays in bounds
-        }
 #pragma unroll
     for (int sg = 0; sg < SEGS; ++sg) {
 #pragma unroll
@@ -757,6 +765,40 @@ struct PresumStream {
     for (int slot = trip * SPT; slot < GS; ++slot)
 #pragma unroll
       for (int sg = 0; sg < SEGS; ++sg) add_bf16x8(v[sg], load(off[sg], slot));
+  }
+};
+
+// The segments of an owned sub-tile of configuration CO, in its epilogue's
+// order (Seg<CO>).
+template <class CO, int GS, int STEPS>
+struct PresumStream : PeerStream<Seg<CO>::COUNT, GS, STEPS> {
+  using SG = Seg<CO>;
+  __device__ __forceinline__ void init(const KArgs& a, int lrow0, int col0, int wm, int wn,
+                                       int lane) {
+    this->start(a);
+    const int col = col0 + SG::col(wn, lane);
+#pragma unroll
+    for (int fm = 0; fm < CO::FM; ++fm)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int it = 0; it < SG::PASSES; ++it)
+          this->set(a, (fm * 2 + h) * SG::PASSES + it, lrow0 + SG::row(wm, lane, fm, h, it), col);
+  }
+};
+
+// The owned half stripe of a gathered-row tile of configuration C (16 owned
+// rows x WN columns per wave, from shard-local row olr), in the order of
+// gather_epilogue: pass it covers rows olr + it*RPI + lane/LPR.
+template <class C, int GS, int STEPS>
+struct GatherStream : PeerStream<Seg<C>::PASSES, GS, STEPS> {
+  using SG = Seg<C>;
+  __device__ __forceinline__ void init(const KArgs& a, int olr, int col0, int wn, int lane) {
+    this->start(a);
+    const int col = col0 + SG::col(wn, lane);
+#pragma unroll
+    for (int it = 0; it < SG::PASSES; ++it)
+      this->set(a, it, olr + it * SG::RPI + lane / SG::LPR, col);
   }
 };
 
@@ -942,6 +984,108 @@ __device__ __forceinline__ void epilogue(const KArgs& a, int shard, int lrow0, i
   }
 }
 
+// Epilogue of a gathered-row tile of row group g (configuration C, 256 rows:
+// gather_row).  PART 0: the send half stripes, bf16 into the send slot of
+// their rows' shard (16 rows that start at a multiple of 16 never straddle
+// two shards); PART 1: the wave's owned half stripe (fm = FM-1, h = 1), out
+// = peer sum (`ps`, ascending slot order from +0) + C, as the owned epilogue
+// adds it.
+template <class C, int PART, class PS>
+__device__ __forceinline__ void gather_epilogue(const KArgs& a, int g, int col0, float* lds_f,
+                                                int wave, int wm, int wn, int lane,
+                                                f32x16 (&acc)[C::FM][C::FN], const PS& ps) {
+  using SG = Seg<C>;
+  static_assert(C::BM == kGatherRows && C::WAVES_M == 2, "two 128-row halves of gathered rows");
+  float* stage = lds_f + wave * 16 * C::EPI_STRIDE;
+  constexpr int LPR = SG::LPR, RPI = SG::RPI, PASSES = SG::PASSES;
+  const int c8 = lane % LPR;
+  const long long col = (long long)col0 + SG::col(wn, lane);
+  const bool col_ok = col < a.N;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool owned_hs = fm == C::FM - 1 && h == 1;
+      if (owned_hs != (PART == 1)) continue;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - 16 * h;
+          stage[row * C::EPI_STRIDE + fn * 32 + (lane & 31)] = acc[fm][fn][r];
+        }
+      wave_lds_sync();
+      if constexpr (PART == 0) {
+        int slot, lrow;
+        gather_send_row(kGatherSendRows * g + 112 * wm + 32 * fm + 16 * h, a.S, slot, lrow);
+#pragma unroll
+        for (int it = 0; it < PASSES; ++it) {
+          const int rr = it * RPI + lane / LPR;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(stage + rr * C::EPI_STRIDE + c8 * 8 + 4);
+          if (col_ok) {
+            const u32x4 o = {pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                             pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3])};
+            store16(a.send + (slot * (long long)a.S + lrow + rr) * a.N + col, o, a.store_nt);
+          }
+        }
+      } else {
+        const int olr = kGatherOwnedRows * g + 16 * wm;
+#pragma unroll
+        for (int it = 0; it < PASSES; ++it) {
+          const int rr = it * RPI + lane / LPR;
+          float* st8 = stage + rr * C::EPI_STRIDE + c8 * 8;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(st8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(st8 + 4);
+          float s8[8] = {ps.v[it][0] + x0[0], ps.v[it][1] + x0[1], ps.v[it][2] + x0[2],
+                         ps.v[it][3] + x0[3], ps.v[it][4] + x1[0], ps.v[it][5] + x1[1],
+                         ps.v[it][6] + x1[2], ps.v[it][7] + x1[3]};
+          if (a.out_bf16) {
+            if (col_ok) store_out(a, (long long)(olr + rr) * a.N + col, s8);
+          } else {
+            *reinterpret_cast<f32x4*>(st8) = f32x4{s8[0], s8[1], s8[2], s8[3]};
+            *reinterpret_cast<f32x4*>(st8 + 4) = f32x4{s8[4], s8[5], s8[6], s8[7]};
+          }
+        }
+        if (!a.out_bf16) {
+          // fp32: dense halves of each row's run of 8*LPR floats, as in the
+          // owned epilogue
+          wave_lds_sync();
+          float* out32 = reinterpret_cast<float*>(a.out);
+          const long long colr = (long long)col0 + wn * C::WN;
+#pragma unroll
+          for (int it = 0; it < PASSES; ++it) {
+            const int rr = it * RPI + lane / LPR;
+            const float* row = stage + rr * C::EPI_STRIDE;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int c = half * 4 * LPR + 4 * c8;
+              const f32x4 y = *reinterpret_cast<const f32x4*>(row + c);
+              if (colr + c < a.N)
+                store16(out32 + (long long)(olr + rr) * a.N + colr + c,
+                        u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                              __float_as_uint(y[3])},
+                        a.store_nt);
+            }
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+// Arrivals of a released gathered-row tile of row group g at every chunk its
+// send rows touch, one (slot, chunk) pair per lane.
+__device__ __forceinline__ void gather_signal(const KArgs& a, int g, int lane) {
+  int n = 0;
+  gather_chunks(g, a.P, a.S, a.chunk_rows, [&](int d, int c) {
+    if (n++ % 64 == lane)
+      signal_chunk(a, d * a.n_chunks + c,
+                   gather_expected_arrivals(d, c, a.S, a.chunk_rows, a.g.Tn));
+  });
+}
+
 // All-gather + GEMM: before a tile of rank tc.shard's rows reads A, one
 // thread waits (the pages' wait primitive) until the ready word of every A
 // chunk the tile's rows touch has reached wait_expected, a signed 32-bit
@@ -1045,7 +1189,8 @@ struct LdsPlan {
 // multiplied into `acc`.  `bg` runs in the background of the main loop; an
 // owned item that takes its peer sum by prefetch (SRC kPeersPrefetch) reads
 // it into `pf`.  On return every stage load has landed and every wave has
-// passed a barrier, so the ring may be refilled.
+// passed a barrier, so the ring may be refilled.  With GA the tile is a
+// gathered-row tile: `lrow0` is its row group and `shard` is unused.
 // The first stages (0 .. S-2) of a work item into the ring b0, b1, ... as
 // main_part issues them; a caller that issues them early (before the previous
 // item's epilogue, so their latency hides behind its stores) then runs
@@ -1076,7 +1221,7 @@ __device__ __forceinline__ void issue_prologue(const KArgs& a, int shard, int lr
   }
 }
 
-template <class C, int GS, int SRC, class BG, class PFT, bool PRE = false>
+template <class C, int GS, int SRC, class BG, class PFT, bool PRE = false, bool GA = false>
 __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, int col0,
                                           unsigned char* b0, unsigned char* b1,
                                           unsigned char* b2, unsigned char* b3, int wave,
@@ -1087,10 +1232,13 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
   shard = uniform_int(shard);
   lrow0 = uniform_int(lrow0);
   col0 = uniform_int(col0);
-  const long long row0 = (long long)shard * a.S + lrow0;
+  // GA (gathered rows): lrow0 is the row group and every A row of the tile
+  // carries its own row of A
+  const long long row0 = GA ? 0 : (long long)shard * a.S + lrow0;
   Loader<C> ld;
   ld.init(a, wave, lane);
-  ld.bind(a, a.S - lrow0, col0);
+  if constexpr (GA) ld.bind_gather(a, lrow0, col0);
+  else ld.bind(a, a.S - lrow0, col0);
   Reader<C> rd;
   rd.init(wm, wn, lane);
   const int nk = (a.K + C::BK - 1) / C::BK;
@@ -1105,9 +1253,9 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
   // prologue: stages 0 .. S-2 (already issued by the caller with PRE)
   constexpr int NQ = C::LOADS;
   if (!PRE && nk > 0) {
-    ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 0), b0, wave);
-    if constexpr (S > 2) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
-    if constexpr (S > 3) ld.template issue<0, NQ>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
+    ld.template issue<0, NQ, GA>(a, ld.stage(a, row0, col0, 0), b0, wave);
+    if constexpr (S > 2) ld.template issue<0, NQ, GA>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
+    if constexpr (S > 3) ld.template issue<0, NQ, GA>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
   }
   if (nk > 0) {
     // Loads complete in issue order, so this leaves stages 1 .. S-2 in
@@ -1131,9 +1279,9 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
     // (they never hold -0).
     for (int kq = 0; kq < nk; kq += S) {
 #define PK_STEP(I)                                                                           \
-  main_stage<C, (I), BG>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd,     \
-                         pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3), \
-                         pick<((I) + 1) % S>(b0, b1, b2, b3), wave, acc, f, bg)
+  main_stage<C, (I), BG, GA>(a, ld, ld.stage(a, row0, col0, (kq + (I) + S - 1) * C::BK), rd, \
+                             pick<(I)>(b0, b1, b2, b3), pick<((I) + S - 1) % S>(b0, b1, b2, b3), \
+                             pick<((I) + 1) % S>(b0, b1, b2, b3), wave, acc, f, bg)
       PK_STEP(0);
       PK_STEP(1);
       if constexpr (S > 2) PK_STEP(2);
@@ -1486,6 +1634,42 @@ __global__ void __launch_bounds__(CS::THREADS)
       }
     }
     return;
+  } else if constexpr (ONE == 3) {
+    static_assert(MODE == kFused && GS == 7 && !SPLIT && CS::BM == kGatherRows &&
+                      CS::WAVES_M == 2 && Seg<CS>::PASSES * 2 * CS::FM == Seg<CS>::COUNT,
+                  "the gathered-row schedule");
+    // Gathered-row tiles in one round (P = 8; the host launches this
+    // instance only when every work item has a workgroup of its own): work
+    // item (g, u) multiplies the 256 rows of row group g (224 send rows, 32
+    // owned rows) by column tile u while its waves sum their owned half
+    // stripes' peer partials in the background, stores the send rows and the
+    // owned rows, then releases once and adds its arrivals.
+    const int wm = wave / CS::WAVES_N, wn = wave % CS::WAVES_N;
+    if (w >= (long long)gather_groups(a.S) * a.g.Tn) return;
+    Grid gg = a.g;
+    gg.Tm = gather_groups(a.S);
+    int grp, u;
+    intra_shard(gg, w, grp, u);
+    const int col0 = u * CS::BN;
+    GatherStream<CS, GS, CS::STAGES * CS::KK> ps;
+    ps.init(a, kGatherOwnedRows * grp + 16 * wm, col0, wn, lane);
+    f32x16 acc[CS::FM][CS::FN];
+    NoPeers nopf;
+    main_part<CS, GS, kSendOnly, decltype(ps), NoPeers, false, true>(
+        a, 0, grp, col0, lds0, lds1, lds2, lds3, wave, lane, ps, nopf, acc);
+    float* stage = reinterpret_cast<float*>(lds0);
+    gather_epilogue<CS, 0>(a, grp, col0, stage, wave, wm, wn, lane, acc, ps);
+    PK_MARK(a, 3);
+    gather_epilogue<CS, 1>(a, grp, col0, stage, wave, wm, wn, lane, acc, ps);
+    PK_MARK(a, 3);
+    wait_vm0();   // this thread's stores have reached the cache
+    __syncthreads();
+    if (wave == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
+      gather_signal(a, grp, lane);
+    }
+    PK_MARK(a, 4);
+    return;
   } else if constexpr (ONE == 1) {
     static_assert(MODE == kFused && SPLIT && GS == 7, "the one-round schedule");
     {
@@ -1804,6 +1988,18 @@ static int launch_as(KArgs& a, const pk_options* o, hipStream_t stream) {
     return PK_ERR_CONFIG;
   if (grid > a.total_tiles) grid = a.total_tiles;
   if (a.timeline && grid + a.n_comm > kTimelineWorkgroups) return PK_ERR_CONFIG;
+  if constexpr (MODE == kFused && __is_same(CS, Cfg1) && __is_same(CO, CfgOwned) && GS == 7) {
+    // The owned split at P = 8 with a workgroup for every gathered-row work
+    // item (S a multiple of 32, 32-bit row offsets into A): the gathered-row
+    // schedule, which needs no sub-tiles.
+    const long long items = (long long)gather_groups(a.S) * a.g.Tn;
+    if (gather_fits(a.P, a.S) && a.n_comm == 0 && items <= grid &&
+        a.M * (long long)a.K * 2 <= (1LL << 31)) {
+      hipLaunchKernelGGL((pk_gemm_rs_fused<CS, CS, MODE, GS, 3>), dim3((unsigned)items),
+                         dim3(CS::THREADS), 0, stream, a);
+      return hipGetLastError() == hipSuccess ? PK_OK : PK_ERR_LAUNCH;
+    }
+  }
   if constexpr (MODE == kFused && !__is_same(CS, CO) && GS == 7) {
     // the owned split in one round with workgroups to spare: its own schedule
     const long long n_send = split_sends(a.g), n_own = split_owned(a.g);
@@ -2293,7 +2489,7 @@ int64_t pk_flags_words(int P, int64_t M, int chunk_rows) {
   const int64_t S = M / P;
   if (S == 0) return 0;
   if (chunk_rows <= 0 || S % chunk_rows != 0) return PK_ERR_SHAPE;
-  return 2 * (int64_t)(P - 1) * (S / chunk_rows);
+  return (1 + pk::kCounterStride) * (int64_t)(P - 1) * (S / chunk_rows);
 }
 
 int pk_validate(const void* A, const void* B, const void* peer_partials, const void* send_bufs,
@@ -2375,6 +2571,35 @@ int64_t pk_chunk_arrivals(int64_t M, int64_t N, int P, int chunk_rows, int confi
   if (chunk_rows <= 0 || S % chunk_rows != 0 || c < 0 || c >= S / chunk_rows) return PK_ERR_SHAPE;
   const pk::CfgInfo& cf = pk::kCfgs[config - 1];
   return pk::expected_arrivals(c, cf.BM, chunk_rows, pk::ceil_div(N, cf.BN));
+}
+
+int pk_gather_rows(int P, int rank, int64_t M, int g, int64_t* rows) {
+  if (P < 1 || P > 64 || rank < 0 || rank >= P) return PK_ERR_RANK;
+  if (M <= 0 || M % P != 0 || !rows) return PK_ERR_SHAPE;
+  const int64_t S = M / P;
+  if (!pk::gather_fits(P, S) || S >= (1LL << 31) || g < 0 || g >= pk::gather_groups(S))
+    return PK_ERR_CONFIG;
+  for (int tr = 0; tr < pk::kGatherRows; ++tr) rows[tr] = pk::gather_row(rank, (int)S, g, tr);
+  return PK_OK;
+}
+
+int pk_gather_arrivals(int64_t M, int64_t N, int P, int chunk_rows, uint32_t* expected,
+                       uint32_t* made) {
+  if (P < 1 || P > 64) return PK_ERR_RANK;
+  if (M <= 0 || M % P != 0 || N <= 0 || !expected || !made) return PK_ERR_SHAPE;
+  const int64_t S = M / P;
+  if (!pk::gather_fits(P, S) || S >= (1LL << 31)) return PK_ERR_CONFIG;
+  if (chunk_rows <= 0 || S % chunk_rows != 0) return PK_ERR_SHAPE;
+  const int n_chunks = (int)(S / chunk_rows), Tn = pk::ceil_div(N, pk::Cfg1::BN);
+  for (int64_t i = 0; i < (int64_t)(P - 1) * n_chunks; ++i) {
+    expected[i] = pk::gather_expected_arrivals((int)(i / n_chunks), (int)(i % n_chunks), (int)S,
+                                               chunk_rows, Tn);
+    made[i] = 0;
+  }
+  for (int g = 0; g < pk::gather_groups(S); ++g)
+    pk::gather_chunks(g, P, (int)S, chunk_rows,
+                      [&](int d, int c) { made[(int64_t)d * n_chunks + c] += (uint32_t)Tn; });
+  return PK_OK;
 }
 
 const char* pk_strerror(int code) {

@@ -164,4 +164,58 @@ PK_HD unsigned expected_arrivals(int c, int BM, int chunk_rows, int Tn) {
   return (unsigned)((r1 / BM - r0 / BM + 1) * (long long)Tn);
 }
 
+// Gathered-row tiles (P = 8, S a multiple of 32; configuration 1's 256 x 256
+// tile).  Instead of whole tiles of one shard, the M rows are cut into S/32
+// row groups of 256: group g holds send rows 224 g .. 224 g + 223 (the P-1
+// send shards' rows one after another in slot order) and owned rows
+// 32 g .. 32 g + 31.  Tile rows 112 .. 127 of each 128-row half h are owned
+// rows 32 g + 16 h .. + 15, the others send rows 224 g + 112 h + r.  Each
+// row group x column tile is one work item, (S/32) * Tn of them, and each
+// holds both send rows and a slice of the owned shard, so no work item is all
+// owned rows.  A 16-row block of send rows that starts at a multiple of 16
+// never straddles two shards (S is a multiple of 32).
+constexpr int kGatherRows = 256, kGatherSendRows = 224, kGatherOwnedRows = 32;
+
+PK_HD bool gather_fits(int P, long long S) { return P == 8 && S > 0 && S % kGatherOwnedRows == 0; }
+PK_HD int gather_groups(long long S) { return (int)(S / kGatherOwnedRows); }
+
+// Send row sr (0 <= sr < (P-1) S, slot order) -> its slot and shard-local row.
+PK_HD void gather_send_row(int sr, int S, int& slot, int& lrow) {
+  slot = sr / S;
+  lrow = sr - slot * S;
+}
+
+// Row of the whole M x K operand A that tile row tr (0 .. 255) of row group g
+// reads.
+PK_HD long long gather_row(int rank, int S, int g, int tr) {
+  const int h = tr >> 7, r = tr & 127;
+  if (r >= 112) return (long long)rank * S + kGatherOwnedRows * g + 16 * h + (r - 112);
+  int slot, lrow;
+  gather_send_row(kGatherSendRows * g + 112 * h + r, S, slot, lrow);
+  return (long long)(slot < rank ? slot : slot + 1) * S + lrow;
+}
+
+// Arrivals chunk c of send slot d waits for under the gathered rows: Tn from
+// every row group whose send rows touch the chunk.
+PK_HD unsigned gather_expected_arrivals(int d, int c, int S, int chunk_rows, int Tn) {
+  const long long r0 = (long long)d * S + (long long)c * chunk_rows;
+  const long long end = (long long)(c + 1) * chunk_rows < S ? (long long)(c + 1) * chunk_rows : S;
+  const long long r1 = (long long)d * S + end - 1;
+  return (unsigned)((r1 / kGatherSendRows - r0 / kGatherSendRows + 1) * (long long)Tn);
+}
+
+// The (slot, chunk) pairs row group g's send rows touch, in order, through
+// visit(slot, chunk); returns how many.
+template <class Visit>
+PK_HD int gather_chunks(int g, int P, int S, int chunk_rows, const Visit& visit) {
+  const int sr0 = kGatherSendRows * g, sr1 = sr0 + kGatherSendRows - 1;
+  int n = 0;
+  for (int d = sr0 / S; d <= sr1 / S && d < P - 1; ++d) {
+    const int lo = sr0 > d * S ? sr0 - d * S : 0;
+    const int hi = sr1 < (d + 1) * S - 1 ? sr1 - d * S : S - 1;
+    for (int c = lo / chunk_rows; c <= hi / chunk_rows; ++c, ++n) visit(d, c);
+  }
+  return n;
+}
+
 }  // namespace pk

@@ -30,10 +30,12 @@
  *    B: bf16 [K][N]; peer_partials and send_bufs: bf16 [P-1][S][N]; out:
  *    fp32 or bf16 [S][N].  Slot j of peer_partials / send_bufs belongs to rank
  *    j if j < rank, else rank j+1 (ascending ranks, skipping `rank`).
- *  - flags: uint32 [pk_flags_words(P, M, chunk_rows)]: first (P-1)*C ready
- *    words (slot-major, C = S / chunk_rows chunks per slot), then (P-1)*C
- *    arrival counters.  Counters must be zero at launch, and are zero again
- *    when the stream reaches the end of the call.  Each call adds exactly 1
+ *  - flags: uint32 [pk_flags_words(P, M, chunk_rows)] = 33*(P-1)*C words:
+ *    first (P-1)*C ready words (slot-major, C = S / chunk_rows chunks per
+ *    slot), then the arrival counters, one per 128-byte line (counter i at
+ *    word (P-1)*C + 32*i, the 31 words after it unused).  Counters (and the
+ *    unused words) must be zero at launch, and are zero again when the stream
+ *    reaches the end of the call.  Each call adds exactly 1
  *    to every ready word (wrapping at 2^32), whatever the tile
  *    configuration or tile order: zero the buffer once, and the n-th call on
  *    it leaves every ready word at n, so a consumer of that call waits for
@@ -104,7 +106,9 @@ typedef struct pk_options {
                            epilogue (P-1 peer reads per element) spreads over many
                            workgroups: 1 on, -1 off, 0 = auto (on when the walk has
                            fewer than two whole tiles per CU).  Tile configuration 1
-                           with P in {2, 4, 8}, and configuration 6 (two workgroups
+                           with P in {2, 4, 8} (at P = 8, when the work fits one
+                           round and S is a multiple of 32, as gathered rows:
+                           pk_gather_rows), and configuration 6 (two workgroups
                            per CU) at P = 8 when every owned sub-tile and send tile
                            fits one grid of two workgroups per CU; elsewhere it
                            stays off. */
@@ -358,10 +362,11 @@ int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
  * whole tile and 0..R-1 for the R sub-tiles of an owned tile under the owned
  * split (owned_split = 1; configurations 1 and 6), where the walk is a list of
  * pairs, each send tile followed by the owned sub-tile that rides with it.
- * When the split's pairs fit in one round of the grid at P = 8, the kernel
- * hands the sub-tiles of every fourth pair (pairs 0, 4, 8, ...) to the
- * workgroups that hold no send tile, and those pairs' workgroups only send;
- * the list is the same.  Configuration 6 hands send tile j to workgroup j of
+ * When the split's pairs fit in one round of the grid at P = 8 and S is a
+ * multiple of 32, the kernel runs the gathered-row schedule instead
+ * (pk_gather_rows); otherwise, in one round, it hands the sub-tiles of every
+ * fourth pair (pairs 0, 4, 8, ...) to the workgroups that hold no send tile,
+ * and those pairs' workgroups only send; the list is the same.  Configuration 6 hands send tile j to workgroup j of
  * the first half of its grid and owned sub-tile j, then send tile half + j,
  * to workgroup j of the second half.  Returns the total number of work items or a
  * negative code.  group_n as in
@@ -369,8 +374,30 @@ int pk_select_config(int64_t M, int64_t N, int64_t K, int P);
 int64_t pk_tile_walk(int64_t M, int64_t N, int P, int rank, int config, int tile_order,
                      int group_n, int owned_split, int32_t* out4, int64_t cap);
 
-/* Arrival count chunk c of every slot waits for, under configuration `config`. */
+/* Arrival count chunk c of every slot waits for, under configuration `config`
+ * with whole tiles or the owned split's sub-tiles (not the gathered rows). */
 int64_t pk_chunk_arrivals(int64_t M, int64_t N, int P, int chunk_rows, int config, int c);
+
+/* Gathered-row schedule (host-only description).  The fused share runs it in
+ * place of the owned split's sub-tiles when configuration 1 takes the owned
+ * split at P = 8, S = M/P is a multiple of 32, the grid holds a workgroup for
+ * every work item, there are no communicator workgroups and M*K*2 <= 2^31.
+ * The M rows are cut into S/32 row groups of 256: group g holds send rows
+ * 224g .. 224g+223 (the P-1 send shards' rows one after another in slot
+ * order) and owned rows 32g .. 32g+31, and work item (g, u) multiplies them
+ * by column tile u ((S/32) x ceil(N/256) items), so every work item stores
+ * send rows and a slice of the owned shard (whose peer partials it sums while
+ * it multiplies) and no workgroup holds a whole owned tile.  The sums, their
+ * order and so every output bit are those of the other schedules; the ready
+ * words rise once per call as there, after a different number of arrivals.
+ * pk_gather_rows writes the rows of A that tile rows 0..255 of group g read
+ * into rows[256]; pk_gather_arrivals writes, for chunk c of send slot d (index
+ * d*(S/chunk_rows) + c), the arrivals the chunk waits for into expected[] and
+ * the arrivals the work items make into made[] (both (P-1)*(S/chunk_rows)).
+ * PK_ERR_CONFIG when (P, S) does not fit the schedule. */
+int pk_gather_rows(int P, int rank, int64_t M, int g, int64_t* rows);
+int pk_gather_arrivals(int64_t M, int64_t N, int P, int chunk_rows, uint32_t* expected,
+                       uint32_t* made);
 
 /* Human-readable name of a return code. */
 const char* pk_strerror(int code);

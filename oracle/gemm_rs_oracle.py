@@ -62,6 +62,19 @@ from dataclasses import dataclass
 
 import numpy as np
 
+# Words per arrival counter in the flags buffer: the pages fix what a counter
+# does, not where it lives; the device keeps each on a 128-byte line of its own.
+COUNTER_LINE_WORDS = 32
+
+
+def flag_words(ready: np.ndarray, counters: np.ndarray) -> np.ndarray:
+    """Flag words in device order: all ready words (slot-major), then each
+    arrival counter at the start of a COUNTER_LINE_WORDS line of its own (the
+    other words of the line zero)."""
+    lines = np.zeros((counters.size, COUNTER_LINE_WORDS), np.uint32)
+    lines[:, 0] = counters.ravel()
+    return np.concatenate([ready.ravel().astype(np.uint32), lines.ravel()])
+
 __all__ = [
     "bf16_bits_to_f64",
     "f64_to_bf16_bits",
@@ -71,6 +84,7 @@ __all__ = [
     "local_partial",
     "local_partial_abs",
     "reduce_scatter_share",
+    "flag_words",
     "gemm_rs_oracle",
     "gemm_rs_elements",
     "partial_elements",
@@ -200,8 +214,8 @@ class OracleResult:
 
     @property
     def flags(self) -> np.ndarray:
-        """Flag words in device order: all ready words, then all counters."""
-        return np.concatenate([self.ready.ravel(), self.counters.ravel()])
+        """Flag words in device order (flag_words)."""
+        return flag_words(self.ready, self.counters)
 
     def out_bf16_bits(self) -> np.ndarray:
         return f64_to_bf16_bits(self.out)

@@ -88,11 +88,12 @@ def host(share: Share):
 
 def expected_flags(w: gen.Workload, chunk_rows: int, calls: int = 1) -> np.ndarray:
     """Closed form after `calls` calls on zeroed flags: every ready word equals
-    `calls` (one signal per chunk per call), every counter 0."""
+    `calls` (one signal per chunk per call), every counter (one per 32-word
+    line) 0."""
     if w.S == 0 or w.P == 1:
         return np.zeros(0, np.uint32)
     n = (w.P - 1) * (w.S // chunk_rows)
-    return np.concatenate([np.full(n, calls, np.uint32), np.zeros(n, np.uint32)])
+    return np.concatenate([np.full(n, calls, np.uint32), np.zeros(32 * n, np.uint32)])
 
 
 def compare_real(res: orc.OracleResult, mag_C, share: Share, n_terms: int):

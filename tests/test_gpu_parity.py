@@ -90,29 +90,46 @@ SPLIT4 = gen.Workload("split4", P=4, rank=1, M=1200, N=328, K=136, chunk_rows=60
                       ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
 SPLIT2 = gen.Workload("split2", P=2, rank=1, M=520, N=264, K=64, chunk_rows=52,
                       ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+# P = 8 in one round: SPLIT8 (S = 512) and GATHER8 (S = 96: three row groups, a
+# ragged last column tile, a partial last K step) take the gathered rows;
+# ONE8 (S = 200, not a multiple of 32) takes the sub-tiles with the spare
+# workgroups.
+GATHER8 = gen.Workload("gather8", P=8, rank=2, M=768, N=1000, K=136, chunk_rows=32,
+                       ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+ONE8 = gen.Workload("one8", P=8, rank=6, M=1600, N=1000, K=136, chunk_rows=40,
+                    ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+SPLITS = [SPLIT8, SPLIT4, SPLIT2, GATHER8, ONE8]
 
 
 @pytest.mark.parametrize("order", [0, 1, 2])
-@pytest.mark.parametrize("w", [SPLIT8, SPLIT4, SPLIT2], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", SPLITS, ids=lambda w: w.name)
 def test_owned_split_integer(w, order):
     _run_and_check(w, "f32", integer=True, order=order, config=1, owned_split=1)
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("w", [SPLIT8, SPLIT4, SPLIT2], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", SPLITS, ids=lambda w: w.name)
 def test_owned_split_real(w, out_dtype):
     _run_and_check(w, out_dtype, integer=False, order=2, config=1, owned_split=1)
 
 
-def test_owned_split_matches_whole_tiles_bitwise():
-    A, B, peers = gen.make_inputs(SPLIT8, DEV, seed=11)
+@pytest.mark.parametrize("w", [SPLIT8, GATHER8, ONE8], ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_owned_split_matches_whole_tiles_bitwise(w, out_dtype):
+    # whole tiles, the P = 8 one-round schedule (gathered rows or sub-tiles),
+    # and the multi-round walk of sub-tiles (a grid of 7 workgroups)
+    A, B, peers = gen.make_inputs(w, DEV, seed=11)
     outs = []
-    for split in (-1, 1):
-        share = H.Share(SPLIT8, "f32")
-        H.run(share, A, B, peers, config=1, owned_split=split)
+    for split, grid in ((-1, 0), (1, 0), (1, 7)):
+        share = H.Share(w, out_dtype)
+        H.run(share, A, B, peers, config=1, owned_split=split, max_workgroups=grid)
         torch.cuda.synchronize()
-        outs.append((share.send.view(torch.int16).clone(), share.out.view(torch.int32).clone()))
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+        assert torch.equal(share.flags.cpu(), torch.from_numpy(
+            H.expected_flags(w, w.chunk_rows).view(np.int32)))
+        outs.append((share.send.view(torch.int16).clone(),
+                     share.out.view(torch.int16 if out_dtype == "bf16" else torch.int32).clone()))
+    for o in outs[1:]:
+        assert torch.equal(outs[0][0], o[0]) and torch.equal(outs[0][1], o[1])
 
 
 @pytest.mark.parametrize("chunk_rows", [8, 40, 200])

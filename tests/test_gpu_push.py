@@ -53,8 +53,7 @@ def test_push_integer_exact(w, order):
     want, ready, counters = orc.push_share(C, before.cpu().numpy().astype(np.float64), w.P,
                                            w.rank, w.chunk_rows)
     assert np.array_equal(accum.cpu().numpy().astype(np.float64), want)
-    assert np.array_equal(flags.cpu().numpy().view(np.uint32),
-                          np.concatenate([ready.ravel(), counters.ravel()]))
+    assert np.array_equal(flags.cpu().numpy().view(np.uint32), orc.flag_words(ready, counters))
 
 
 @pytest.mark.parametrize("integer", [True, False])

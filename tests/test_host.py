@@ -37,9 +37,10 @@ def test_version_and_strerror():
 
 
 def test_flags_words():
-    assert pk.pk_flags_words(8, 4096, 128) == 2 * 7 * 4
-    assert pk.pk_flags_words(8, 32768, 256) == 2 * 7 * 16
-    assert pk.pk_flags_words(2, 256, 64) == 2 * 1 * 2
+    # ready words, then one 32-word line per arrival counter
+    assert pk.pk_flags_words(8, 4096, 128) == 33 * 7 * 4
+    assert pk.pk_flags_words(8, 32768, 256) == 33 * 7 * 16
+    assert pk.pk_flags_words(2, 256, 64) == 33 * 1 * 2
     assert pk.pk_flags_words(1, 256, 64) == 0
     assert pk.pk_flags_words(4, 0, 0) == 0
     with pytest.raises(pk.PkError):
@@ -294,3 +295,60 @@ def test_intercu_reduce_rejects_before_any_hip_call(kw, code):
         a["M"], a["N"], a["K"], a["P"], a["rank"], a["chunk_rows"], a["tile_order"],
         a["out_bf16"], ctypes.c_uint32(a["expected"]), a["n_comm"], a["spin"], None, None)
     assert rc == code
+
+
+# Gathered-row schedule (P = 8, S a multiple of 32): each row group of 256
+# tile rows holds 224 send rows in slot order and 32 owned rows.
+GATHER_SHAPES = [(4096, 4096, 8, 3, 128), (4096, 768, 8, 5, 64), (768, 1000, 8, 2, 32),
+                 (1536, 328, 8, 0, 96), (256, 256, 8, 7, 32)]
+
+
+@pytest.mark.parametrize("M,N,P,rank,cr", GATHER_SHAPES)
+def test_gathered_rows_cover_every_row_once_in_slot_order(M, N, P, rank, cr):
+    S = M // P
+    groups = [pk.pk_gather_rows(P, rank, M, g) for g in range(S // 32)]
+    assert sorted(np.concatenate(groups).tolist()) == list(range(M))
+    send = []
+    for g, r in enumerate(groups):
+        for h in range(2):
+            # tile rows 112..127 of each half: owned rows 32 g + 16 h ..
+            assert (r[128 * h + 112:128 * h + 128] == rank * S + 32 * g + 16 * h + np.arange(16)).all()
+            # the epilogue stores 16-row blocks of send rows: consecutive rows of one shard
+            for b in range(7):
+                blk = r[128 * h + 16 * b:128 * h + 16 * b + 16]
+                assert (np.diff(blk) == 1).all() and blk[0] // S == blk[-1] // S != rank
+            send.extend(r[128 * h:128 * h + 112].tolist())
+    # all send rows, shard by shard in slot order (the owner skipped)
+    assert send == [d * S + i for d in range(P) if d != rank for i in range(S)]
+
+
+@pytest.mark.parametrize("M,N,P,rank,cr", GATHER_SHAPES)
+def test_gathered_arrivals_are_what_the_work_items_make(M, N, P, rank, cr):
+    exp, made = pk.pk_gather_arrivals(M, N, P, cr)
+    assert exp.shape == (P - 1, M // P // cr)
+    assert (exp > 0).all() and (exp == made).all()
+
+
+def test_gathered_arrivals_hand_counted():
+    # S = 512, 16 column tiles, chunks of 128 rows: send rows 0..223 are group 0,
+    # 224..447 group 1, 448..671 group 2, ...
+    exp, _ = pk.pk_gather_arrivals(4096, 4096, 8, 128)
+    assert exp[0, 0] == 16          # rows 0..127 of slot 0: group 0
+    assert exp[0, 1] == 32          # rows 128..255: groups 0 and 1
+    assert exp[0, 3] == 32          # rows 384..511: groups 1 and 2
+    assert exp[1, 0] == 16          # send rows 512..639: group 2
+    assert exp[6, 3] == 16          # send rows 3456..3583: group 15 only
+    rows = pk.pk_gather_rows(8, 3, 4096, 0)
+    assert rows[0] == 0 and rows[111] == 111 and rows[112] == 3 * 512 and rows[128] == 112
+    assert rows[240] == 3 * 512 + 16
+
+
+def test_gathered_rows_reject_shapes_that_do_not_fit():
+    with pytest.raises(pk.PkError):
+        pk.pk_gather_rows(4, 0, 1024, 0)          # P != 8
+    with pytest.raises(pk.PkError):
+        pk.pk_gather_rows(8, 0, 8 * 200, 0)       # S % 32
+    with pytest.raises(pk.PkError):
+        pk.pk_gather_rows(8, 0, 4096, 16)         # group past S / 32
+    with pytest.raises(pk.PkError):
+        pk.pk_gather_arrivals(8 * 200, 512, 8, 40)

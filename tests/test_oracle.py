@@ -275,7 +275,10 @@ def test_flags_closed_form():
     res = orc.gemm_rs_oracle(_bits(A), _bits(B), np.zeros((3, 16, 8), np.uint16), 4, 3, 4)
     assert res.ready.shape == (3, 4) and np.all(res.ready == 1)
     assert res.counters.shape == (3, 4) and np.all(res.counters == 0)
-    assert np.array_equal(res.flags, np.array([1] * 12 + [0] * 12, np.uint32))
+    # device order: 12 ready words, then 12 counters, one per 32-word line
+    assert np.array_equal(res.flags, np.array([1] * 12 + [0] * (12 * 32), np.uint32))
+    res.counters[1, 2] = 5   # a counter sits at the start of its own line
+    assert res.flags[12 + 32 * 6] == 5 and res.flags.sum() == 12 + 5
 
 
 def test_ready_words_count_calls():
