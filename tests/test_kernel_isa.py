@@ -10,6 +10,9 @@ from the main loop can break without a word from the compiler:
 * Every instance's main loop is one straight-line block holding a whole trip
   of the ring: FM * FN * (BK / 16) * STAGES MFMAs of its configuration (and
   of the owned sub-tile configuration where the instance has one).
+* No instance spills vector registers to scratch memory beyond the few
+  listed below (two copies of a main loop body with its 256 accumulators
+  have made the compiler spill a few hundred).
 """
 import os
 import re
@@ -47,12 +50,16 @@ def kernels(tmp_path_factory):
     dem = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True,
                          text=True).stdout.splitlines()
     res = {}
+    meta = text[text.index("amdhsa.kernels"):]
     for mangled, name in zip(names, dem):
         if "pk_gemm_rs_fused<" not in name:
             continue
         i = text.index(mangled + ":")
         body = text[i:text.index(".Lfunc_end", i)]
-        res[name] = re.split(r"\n\.LBB\S+:", body)
+        j = meta.index(".name:           " + mangled + "\n")
+        entry = meta[meta.rfind("\n  - ", 0, j):meta.find("\n  - ", j)]
+        spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", entry)
+        res[name] = (re.split(r"\n\.LBB\S+:", body), int(spill.group(1)) if spill else -1)
     assert res, "no pk_gemm_rs_fused instance in the assembly"
     return res
 
@@ -64,7 +71,7 @@ def _trip_mfmas(cfg):
 
 def test_no_lane_loop_around_stage_loads(kernels):
     bad = []
-    for name, blocks in kernels.items():
+    for name, (blocks, _) in kernels.items():
         n = sum(1 for b in blocks
                 if "offen lds" in b and "v_readfirstlane" in b and "s_cbranch_execnz" in b)
         if n:
@@ -74,7 +81,7 @@ def test_no_lane_loop_around_stage_loads(kernels):
 
 def test_main_loop_trip_is_one_block(kernels):
     bad = []
-    for name, blocks in kernels.items():
+    for name, (blocks, _) in kernels.items():
         counts = [b.count("v_mfma") for b in blocks]
         cs, co = CFG.findall(name)[:2]
         for cfg in {cs, co}:
@@ -82,4 +89,20 @@ def test_main_loop_trip_is_one_block(kernels):
             if want not in counts:
                 bad.append(f"{name}: no block of {want} MFMAs for Cfg<{', '.join(cfg)}> "
                            f"(largest {max(counts)})")
+    assert not bad, "\n".join(bad)
+
+
+# The multi-round walk of send tiles paired with owned sub-tiles (the owned
+# split when it does not fit one round) spills 4 VGPRs, its scalar spills
+# having taken vector lanes: 2 scratch loads per 128-MFMA trip of its main
+# loop.  Every other instance spills none.
+SPILL_ALLOWED = {"Cfg<256, 256, 2, 2, 32, 4, 1>, pk::Cfg<64, 128, 2, 2, 64, 4, 1>, 0, 7, 0>": 4}
+
+
+def test_no_vector_register_spills(kernels):
+    bad = []
+    for name, (_, n) in kernels.items():
+        allowed = max([v for k, v in SPILL_ALLOWED.items() if k in name], default=0)
+        if n < 0 or n > allowed:
+            bad.append(f"{name}: {n} VGPRs spilled (allowed {allowed})")
     assert not bad, "\n".join(bad)
