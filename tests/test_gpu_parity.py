@@ -98,7 +98,10 @@ GATHER8 = gen.Workload("gather8", P=8, rank=2, M=768, N=1000, K=136, chunk_rows=
                        ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
 ONE8 = gen.Workload("one8", P=8, rank=6, M=1600, N=1000, K=136, chunk_rows=40,
                     ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
-SPLITS = [SPLIT8, SPLIT4, SPLIT2, GATHER8, ONE8]
+# gathered rows with one k16 step of K (a single partial stage)
+GATHER8K8 = gen.Workload("gather8k8", P=8, rank=0, M=1024, N=264, K=8, chunk_rows=64,
+                         ab_dist="uniform1", peer_dist="uniform8", out_dtype="f32")
+SPLITS = [SPLIT8, SPLIT4, SPLIT2, GATHER8, ONE8, GATHER8K8]
 
 
 @pytest.mark.parametrize("order", [0, 1, 2])
@@ -137,8 +140,9 @@ def test_chunk_sizes_ragged(chunk_rows):
     _run_and_check(RAGGED, "f32", integer=True, chunk_rows=chunk_rows)
 
 
-def test_k_zero_gives_peer_sum():
-    w = gen.Workload("k0", P=4, rank=2, M=256, N=64, K=0, chunk_rows=16,
+@pytest.mark.parametrize("P,rank,M", [(4, 2, 256), (8, 5, 512)])   # P = 8: gathered rows
+def test_k_zero_gives_peer_sum(P, rank, M):
+    w = gen.Workload("k0", P=P, rank=rank, M=M, N=64, K=0, chunk_rows=16,
                      ab_dist="uniform1", peer_dist="int", out_dtype="f32")
     A = torch.empty((w.M, 0), dtype=torch.bfloat16, device=DEV)
     B = torch.empty((0, w.N), dtype=torch.bfloat16, device=DEV)
