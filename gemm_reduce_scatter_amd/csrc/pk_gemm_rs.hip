@@ -1239,24 +1239,27 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
   ld.init(a, wave, lane);
   if constexpr (GA) ld.bind_gather(a, lrow0, col0);
   else ld.bind(a, a.S - lrow0, col0);
-  Reader<C> rd;
-  rd.init(wm, wn, lane);
   const int nk = (a.K + C::BK - 1) / C::BK;
 
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // prologue: stages 0 .. S-2 (already issued by the caller with PRE)
+  // prologue: stages 0 .. S-2 (already issued by the caller with PRE).  The
+  // loads go out first; zeroing the accumulators (one instruction per
+  // register, some 256 per lane) and the reader's set-up then run while
+  // they are in flight instead of delaying them.
   constexpr int NQ = C::LOADS;
   if (!PRE && nk > 0) {
     ld.template issue<0, NQ, GA>(a, ld.stage(a, row0, col0, 0), b0, wave);
     if constexpr (S > 2) ld.template issue<0, NQ, GA>(a, ld.stage(a, row0, col0, C::BK), b1, wave);
     if constexpr (S > 3) ld.template issue<0, NQ, GA>(a, ld.stage(a, row0, col0, 2 * C::BK), b2, wave);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  Reader<C> rd;
+  rd.init(wm, wn, lane);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   if (nk > 0) {
     // Loads complete in issue order, so this leaves stages 1 .. S-2 in
     // flight; older stores of the previous item are retired too (with PRE,
@@ -1642,8 +1645,8 @@ __global__ void __launch_bounds__(CS::THREADS)
     // instance only when every work item has a workgroup of its own): work
     // item (g, u) multiplies the 256 rows of row group g (224 send rows, 32
     // owned rows) by column tile u while its waves sum their owned half
-    // stripes' peer partials in the background, stores the send rows and the
-    // owned rows, then releases once and adds its arrivals.
+    // stripes' peer partials in the background, stores the send rows,
+    // releases them once and adds its arrivals, then stores the owned rows.
     const int wm = wave / CS::WAVES_N, wn = wave % CS::WAVES_N;
     if (w >= (long long)gather_groups(a.S) * a.g.Tn) return;
     Grid gg = a.g;
@@ -1660,8 +1663,9 @@ __global__ void __launch_bounds__(CS::THREADS)
     float* stage = reinterpret_cast<float*>(lds0);
     gather_epilogue<CS, 0>(a, grp, col0, stage, wave, wm, wn, lane, acc, ps);
     PK_MARK(a, 3);
-    gather_epilogue<CS, 1>(a, grp, col0, stage, wave, wm, wn, lane, acc, ps);
-    PK_MARK(a, 3);
+    // The send rows are released and signalled before the owned rows are
+    // stored, so the release waits for none of those stores and the other
+    // waves store theirs while wave 0 signals.
     wait_vm0();   // this thread's stores have reached the cache
     __syncthreads();
     if (wave == 0) {
@@ -1669,6 +1673,8 @@ __global__ void __launch_bounds__(CS::THREADS)
       gather_signal(a, grp, lane);
     }
     PK_MARK(a, 4);
+    gather_epilogue<CS, 1>(a, grp, col0, stage, wave, wm, wn, lane, acc, ps);
+    PK_MARK(a, 3);
     return;
   } else if constexpr (ONE == 1) {
     static_assert(MODE == kFused && SPLIT && GS == 7, "the one-round schedule");

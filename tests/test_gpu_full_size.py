@@ -55,28 +55,28 @@ def _edge_tiles(w, tile=256):
     return tiles
 
 
+@pytest.mark.parametrize("integer", [False, True], ids=["real", "integer_twin"])
 @pytest.mark.parametrize("name", ["near_threshold", "compute_bound", "large_k"])
-def test_large_workload_stratified(name):
+def test_large_workload_stratified(name, integer):
     w = gen.WORKLOADS[name]
-    for integer in (False, True):
-        kind = "integer twin" if integer else "real"
-        print(f"[{name} {kind}] generating", flush=True)
-        A, B, peers = gen.make_inputs(w, DEV, seed=1 if integer else 0, integer=integer)
-        share = H.Share(w, w.out_dtype)
-        print(f"[{name} {kind}] running", flush=True)
-        H.run(share, A, B, peers)
-        torch.cuda.synchronize()
-        assert np.array_equal(share.flags.cpu().numpy().view(np.uint32),
-                              H.expected_flags(w, w.chunk_rows))
-        assert share.canaries_intact()
-        rows, cols = H.stratified_positions(w, seed=10 + integer)
-        print(f"[{name} {kind}] checking {rows.size} positions", flush=True)
-        st = H.check_positions(w, A, B, peers, share, rows, cols, integer)
-        H.check_tiles(w, A, B, peers, share, _edge_tiles(w), integer)
-        st["complete_tiles"] = len(_edge_tiles(w))
-        H.record(f"{name} {kind}", st)
-        del A, B, peers, share
-        torch.cuda.empty_cache()
+    kind = "integer twin" if integer else "real"
+    print(f"[{name} {kind}] generating", flush=True)
+    A, B, peers = gen.make_inputs(w, DEV, seed=1 if integer else 0, integer=integer)
+    share = H.Share(w, w.out_dtype)
+    print(f"[{name} {kind}] running", flush=True)
+    H.run(share, A, B, peers)
+    torch.cuda.synchronize()
+    assert np.array_equal(share.flags.cpu().numpy().view(np.uint32),
+                          H.expected_flags(w, w.chunk_rows))
+    assert share.canaries_intact()
+    rows, cols = H.stratified_positions(w, seed=10 + integer)
+    print(f"[{name} {kind}] checking {rows.size} positions", flush=True)
+    st = H.check_positions(w, A, B, peers, share, rows, cols, integer)
+    H.check_tiles(w, A, B, peers, share, _edge_tiles(w), integer)
+    st["complete_tiles"] = len(_edge_tiles(w))
+    H.record(f"{name} {kind}", st)
+    del A, B, peers, share
+    torch.cuda.empty_cache()
 
 
 def _virtual_ranks(w, seed, orders=(0, 1, 2)):
