@@ -324,12 +324,16 @@ struct Loader {
 
   // Gathered rows: the A row of load q is tile row a_row + q*WAVES*A_RPL of
   // row group g, at its own row of A (gather_row); the stage descriptor then
-  // starts at row 0 and the loads take no row step.
-  __device__ __forceinline__ void bind_gather(const KArgs& a, int g, int col0) {
+  // starts at row 0 and the loads take no row step.  A load covers one block
+  // of 16 tile rows, which are 16 consecutive rows of A, so the block's first
+  // row is worked out once per wave (scalar) and each lane adds its offset.
+  __device__ __forceinline__ void bind_gather(const KArgs& a, int g, int col0, int wave, int lane) {
+    static_assert(C::A_RPL == 16, "a load covers one 16-row block");
 #pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q)
-      a_vo[q] = (uint32_t)(gather_row(a.rank, a.S, g, a_row + q * C::WAVES * C::A_RPL) * a.K +
-                           a_kc) * 2u;
+    for (int q = 0; q < C::A_LOADS; ++q) {
+      const long long r0 = gather_row(a.rank, a.S, g, (q * C::WAVES + wave) * C::A_RPL);
+      a_vo[q] = (uint32_t)((r0 + lane / C::A_CPR) * a.K + a_kc) * 2u;
+    }
     b_vo = col0 + b_nc < a.N ? b_off : kOffNone;
   }
 
@@ -1237,7 +1241,7 @@ __device__ __forceinline__ void main_part(const KArgs& a, int shard, int lrow0, 
   const long long row0 = GA ? 0 : (long long)shard * a.S + lrow0;
   Loader<C> ld;
   ld.init(a, wave, lane);
-  if constexpr (GA) ld.bind_gather(a, lrow0, col0);
+  if constexpr (GA) ld.bind_gather(a, lrow0, col0, wave, lane);
   else ld.bind(a, a.S - lrow0, col0);
   const int nk = (a.K + C::BK - 1) / C::BK;
 
