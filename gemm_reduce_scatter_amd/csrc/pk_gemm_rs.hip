@@ -563,17 +563,24 @@ __device__ __forceinline__ unsigned char* pick(unsigned char* b0, unsigned char*
 // launch at different chunks then do not queue behind each other at one line
 // (measured 2-3 us of the comm-dominant share with all counters in one line).
 constexpr int kCounterStride = 32;
+__device__ __forceinline__ uint32_t* chunk_counter(const KArgs& a, int idx) {
+  return a.flags + (long long)(a.P - 1) * a.n_chunks + (long long)kCounterStride * idx;
+}
+// One arrival at chunk idx; returns the count before it.
+__device__ __forceinline__ uint32_t arrive_chunk(const KArgs& a, int idx) {
+  return __hip_atomic_fetch_add(chunk_counter(a, idx), 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+// The arrival that completed chunk idx: acquire, raise the ready word, reset
+// the counter.
+__device__ __forceinline__ void complete_chunk(const KArgs& a, int idx) {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __hip_atomic_fetch_add(&a.flags[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(chunk_counter(a, idx), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.ready_clock) a.ready_clock[idx] = wall_clock64();
+}
 __device__ __forceinline__ void signal_chunk(const KArgs& a, int idx, uint32_t want) {
-  uint32_t* ready = a.flags;
-  uint32_t* counter = a.flags + (long long)(a.P - 1) * a.n_chunks + (long long)kCounterStride * idx;
-  const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-  if (old + 1u == want) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __hip_atomic_fetch_add(&ready[idx], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (a.ready_clock) a.ready_clock[idx] = wall_clock64();
-  }
+  if (arrive_chunk(a, idx) + 1u == want) complete_chunk(a, idx);
 }
 
 // Arrivals of a batch of finished send tiles, spread over the lanes of one
@@ -1079,15 +1086,41 @@ __device__ __forceinline__ void gather_epilogue(const KArgs& a, int g, int col0,
   }
 }
 
-// Arrivals of a released gathered-row tile of row group g at every chunk its
-// send rows touch, one (slot, chunk) pair per lane.
-__device__ __forceinline__ void gather_signal(const KArgs& a, int g, int lane) {
-  int n = 0;
+// Release of a gathered-row tile of row group g, whose stores every thread has
+// waited for and met the others at a barrier after: wave 0 releases and adds
+// the tile's arrivals at every chunk its send rows touch, one (slot, chunk)
+// pair per lane.  Wave 0 meets the other waves at one more barrier as soon as
+// its first 64 arrivals are issued, so the stores the others go on to issue
+// queue behind those arrivals rather than ahead of them (measured 3 % of the
+// comm-dominant share); it looks at what they returned after the barrier.
+// Pairs past the first 64 (chunks of a few rows only) follow one per lane.
+// Every wave of the workgroup calls it.
+__device__ __forceinline__ void gather_release(const KArgs& a, int g, int wave, int lane) {
+  if (wave != 0) {
+    __builtin_amdgcn_s_barrier();
+    return;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
+  int idx = -1, n = 0;
+  uint32_t want = 0;
   gather_chunks(g, a.P, a.S, a.chunk_rows, [&](int d, int c) {
-    if (n++ % 64 == lane)
-      signal_chunk(a, d * a.n_chunks + c,
-                   gather_expected_arrivals(d, c, a.S, a.chunk_rows, a.g.Tn));
+    if (n++ == lane) {
+      idx = d * a.n_chunks + c;
+      want = gather_expected_arrivals(d, c, a.S, a.chunk_rows, a.g.Tn);
+    }
   });
+  const uint32_t old = idx >= 0 ? arrive_chunk(a, idx) : 0u;
+  __builtin_amdgcn_s_barrier();
+  if (idx >= 0 && old + 1u == want) complete_chunk(a, idx);
+  if (n > 64) {
+    int m = 0;
+    gather_chunks(g, a.P, a.S, a.chunk_rows, [&](int d, int c) {
+      if (m >= 64 && m % 64 == lane)
+        signal_chunk(a, d * a.n_chunks + c,
+                     gather_expected_arrivals(d, c, a.S, a.chunk_rows, a.g.Tn));
+      ++m;
+    });
+  }
 }
 
 // All-gather + GEMM: before a tile of rank tc.shard's rows reads A, one
@@ -1672,10 +1705,7 @@ __global__ void __launch_bounds__(CS::THREADS)
     // waves store theirs while wave 0 signals.
     wait_vm0();   // this thread's stores have reached the cache
     __syncthreads();
-    if (wave == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
-      gather_signal(a, grp, lane);
-    }
+    gather_release(a, grp, wave, lane);
     PK_MARK(a, 4);
     gather_epilogue<CS, 1>(a, grp, col0, stage, wave, wm, wn, lane, acc, ps);
     PK_MARK(a, 3);
