@@ -116,6 +116,13 @@ def test_owned_split_real(w, out_dtype):
     _run_and_check(w, out_dtype, integer=False, order=2, config=1, owned_split=1)
 
 
+@pytest.mark.parametrize("chunk_rows", [2, 4, 96])
+def test_gathered_rows_chunk_sizes(chunk_rows):
+    # chunks of 2 rows: a row group's 224 send rows touch 113 chunks, past the
+    # 64 arrivals a wave issues at once
+    _run_and_check(GATHER8, "f32", integer=True, chunk_rows=chunk_rows, config=1, owned_split=1)
+
+
 @pytest.mark.parametrize("w", [SPLIT8, GATHER8, ONE8], ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_owned_split_matches_whole_tiles_bitwise(w, out_dtype):
