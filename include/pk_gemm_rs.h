@@ -111,7 +111,8 @@ typedef struct pk_options {
                            pk_gather_rows), and configuration 6 (two workgroups
                            per CU) at P = 8 when every owned sub-tile and send tile
                            fits one grid of two workgroups per CU; elsewhere it
-                           stays off. */
+                           stays off, except that configuration 6 with 1 where its
+                           schedule does not fit is PK_ERR_CONFIG. */
   int signal_batch;     /* finished send tiles of a workgroup whose chunk arrivals
                            share one device-scope release, 0 = auto (8).  Larger
                            batches cost fewer cache writebacks and raise ready words

@@ -123,6 +123,63 @@ def test_gathered_rows_chunk_sizes(chunk_rows):
     _run_and_check(GATHER8, "f32", integer=True, chunk_rows=chunk_rows, config=1, owned_split=1)
 
 
+def _random_cases(n, seed=20261203):
+    """Seeded shapes drawn over the planner's choices: P = 2, 4 or 8 (P = 8
+    with S a multiple of 32 takes the gathered rows, otherwise the sub-tiles),
+    ragged N and K, any chunk size that divides S, every order, the default or
+    a forced configuration and owned split."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        P = int(rng.choice([2, 4, 8, 8, 8]))
+        S = int(rng.choice([32, 64, 96, 104, 160, 200, 256, 288, 320]))
+        divs = [d for d in range(1, S + 1) if S % d == 0]
+        chunk = int(rng.choice(divs))
+        N = 8 * int(rng.integers(1, 140))
+        K = 8 * int(rng.integers(0, 40))
+        opts = {}
+        cfg = int(rng.choice([0, 1, 1, 1, 4, 6]))
+        if cfg:
+            opts["config"] = cfg
+        # configuration 6 rejects a forced split it cannot run
+        split = int(rng.choice([0, -1] if cfg == 6 else [0, 1, 1, -1]))
+        if split:
+            opts["owned_split"] = split
+        w = gen.Workload(f"rand{i}", P=P, rank=int(rng.integers(0, P)), M=P * S, N=N, K=K,
+                         chunk_rows=chunk, ab_dist="uniform1", peer_dist="uniform8",
+                         out_dtype=str(rng.choice(["f32", "bf16"])))
+        cases.append((w, int(rng.integers(0, 3)), opts))
+    return cases
+
+
+def _random_gather_cases(n, seed=31):
+    """Seeded shapes that take the gathered rows (P = 8, S a multiple of 32,
+    configuration 1 with the owned split, every (row group, column tile) item
+    on a workgroup of its own)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        S = 32 * int(rng.integers(1, 21))
+        tn_max = max(1, min(5, 256 // (S // 32)))
+        N = 8 * int(rng.integers(1, 32 * tn_max + 1))
+        divs = [d for d in range(1, S + 1) if S % d == 0]
+        w = gen.Workload(f"rgather{i}", P=8, rank=int(rng.integers(0, 8)), M=8 * S, N=N,
+                         K=8 * int(rng.integers(0, 48)), chunk_rows=int(rng.choice(divs)),
+                         ab_dist="uniform1", peer_dist="uniform8",
+                         out_dtype=str(rng.choice(["f32", "bf16"])))
+        cases.append((w, int(rng.integers(0, 3)), {"config": 1, "owned_split": 1}))
+    return cases
+
+
+RANDOM_CASES = _random_cases(16) + _random_gather_cases(8)
+
+
+@pytest.mark.parametrize("w,order,opts", RANDOM_CASES, ids=lambda c: getattr(c, "name", None))
+def test_random_shapes_integer_exact(w, order, opts):
+    print(w, order, opts, flush=True)
+    _run_and_check(w, w.out_dtype, integer=True, order=order, **opts)
+
+
 @pytest.mark.parametrize("w", [SPLIT8, GATHER8, ONE8], ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_owned_split_matches_whole_tiles_bitwise(w, out_dtype):

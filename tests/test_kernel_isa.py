@@ -93,10 +93,12 @@ def test_main_loop_trip_is_one_block(kernels):
 
 
 # The multi-round walk of send tiles paired with owned sub-tiles (the owned
-# split when it does not fit one round) spills 4 VGPRs, its scalar spills
-# having taken vector lanes: 2 scratch loads per 128-MFMA trip of its main
-# loop.  Every other instance spills none.
-SPILL_ALLOWED = {"Cfg<256, 256, 2, 2, 32, 4, 1>, pk::Cfg<64, 128, 2, 2, 64, 4, 1>, 0, 7, 0>": 4}
+# split when it does not fit one round) spills 7 VGPRs, its scalar spills
+# having taken vector lanes: 2 scratch loads per 128-MFMA trip of one of its
+# main loops, the rest outside the loops (4 before the stage loads were issued
+# ahead of the accumulator zeroing, with the same 2 per trip).  Every other
+# instance spills none.
+SPILL_ALLOWED = {"Cfg<256, 256, 2, 2, 32, 4, 1>, pk::Cfg<64, 128, 2, 2, 64, 4, 1>, 0, 7, 0>": 7}
 
 
 def test_no_vector_register_spills(kernels):
