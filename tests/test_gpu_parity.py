@@ -180,6 +180,12 @@ def test_random_shapes_integer_exact(w, order, opts):
     _run_and_check(w, w.out_dtype, integer=True, order=order, **opts)
 
 
+@pytest.mark.parametrize("w,order,opts", RANDOM_CASES[::2], ids=lambda c: getattr(c, "name", None))
+def test_random_shapes_real(w, order, opts):
+    print(w, order, opts, flush=True)
+    print(_run_and_check(w, w.out_dtype, integer=False, seed=7, order=order, **opts))
+
+
 @pytest.mark.parametrize("w", [SPLIT8, GATHER8, ONE8], ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_owned_split_matches_whole_tiles_bitwise(w, out_dtype):
