@@ -329,6 +329,35 @@ def test_gathered_arrivals_are_what_the_work_items_make(M, N, P, rank, cr):
     assert (exp > 0).all() and (exp == made).all()
 
 
+def _gather_random_shapes(n, seed=5):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        S = 32 * int(rng.integers(1, 40))
+        divs = [d for d in range(1, S + 1) if S % d == 0]
+        out.append((8 * S, 8 * int(rng.integers(1, 200)), 8, int(rng.integers(0, 8)),
+                    int(rng.choice(divs))))
+    return out
+
+
+@pytest.mark.parametrize("M,N,P,rank,cr", _gather_random_shapes(12))
+def test_gathered_arrivals_brute_force(M, N, P, rank, cr):
+    """Arrivals counted from the row lists themselves: a chunk waits for one
+    arrival per column tile from every row group whose rows hold one of its
+    rows."""
+    S, Tn = M // P, -(-N // 256)
+    want = np.zeros((P - 1, S // cr), np.int64)
+    for g in range(S // 32):
+        rows = pk.pk_gather_rows(P, rank, M, g)
+        shard, lrow = rows // S, rows % S
+        send = shard != rank
+        slot = np.where(shard[send] < rank, shard[send], shard[send] - 1)
+        for d, c in set(zip(slot.tolist(), (lrow[send] // cr).tolist())):
+            want[d, c] += Tn
+    exp, made = pk.pk_gather_arrivals(M, N, P, cr)
+    assert np.array_equal(exp, want) and np.array_equal(made, want)
+
+
 def test_gathered_arrivals_hand_counted():
     # S = 512, 16 column tiles, chunks of 128 rows: send rows 0..223 are group 0,
     # 224..447 group 1, 448..671 group 2, ...
