@@ -1095,12 +1095,19 @@ __device__ __forceinline__ void gather_epilogue(const KArgs& a, int g, int col0,
 // comm-dominant share); it looks at what they returned after the barrier.
 // Pairs past the first 64 (chunks of a few rows only) follow one per lane.
 // Every wave of the workgroup calls it.
+// The send rows were stored with store16, which writes through the L2 at
+// system scope (sc0 sc1), and every wave has waited for its stores to complete
+// before the barrier ahead of this call: they are already visible beyond the
+// L2, so the release only has to keep the arrivals behind them, which a
+// workgroup-scope release does (a wait, no writeback of the L2, measured 1 us
+// of the comm-dominant share).  The arrival that completes a chunk still
+// acquires and raises the ready word with a device-scope release.
 __device__ __forceinline__ void gather_release(const KArgs& a, int g, int wave, int lane) {
   if (wave != 0) {
     __builtin_amdgcn_s_barrier();
     return;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // ... and the whole cache, memory
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   int idx = -1, n = 0;
   uint32_t want = 0;
   gather_chunks(g, a.P, a.S, a.chunk_rows, [&](int d, int c) {

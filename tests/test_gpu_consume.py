@@ -68,9 +68,12 @@ def test_consume_after_the_producer():
     assert torch.equal(share.flags, flags_before)          # the consumer writes no flag
 
 
-def test_consume_concurrently_with_the_producer():
+@pytest.mark.parametrize("config", [0, 1])
+def test_consume_concurrently_with_the_producer(config):
     """Producer and consumer on two streams at once; the producer leaves 16
-    CUs to the consumer.  Every chunk must be seen after its word rose."""
+    CUs to the consumer.  Every chunk must be seen after its word rose.
+    Configuration 0 lets the library choose (64 x 64 tiles here); 1 runs the
+    gathered rows (P = 8, S = 256: 8 row groups x 4 column tiles)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     share = H.Share(W, "f32")
     dest, status, observed = _staging()
@@ -79,7 +82,9 @@ def test_consume_concurrently_with_the_producer():
     A, B, peers = gen.make_inputs(W, DEV, seed=3, integer=True)
     torch.cuda.synchronize()
     s_prod, s_cons = torch.cuda.Stream(), torch.cuda.Stream()
-    H.run(share, A, B, peers, stream=s_prod, max_workgroups=max(cus - 16, 1), ready_clock=clock)
+    opts = {"config": config} if config else {}
+    H.run(share, A, B, peers, stream=s_prod, max_workgroups=max(cus - 16, 1), ready_clock=clock,
+          **opts)
     pk.pk_rs_consume(share.flags, share.send, dest, W.M, W.N, W.P, W.chunk_rows, 1, status,
                      observed, spin_limit=1 << 16, max_workgroups=16, stream=s_cons)
     torch.cuda.synchronize()
