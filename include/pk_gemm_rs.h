@@ -40,6 +40,10 @@
  *    configuration or tile order: zero the buffer once, and the n-th call on
  *    it leaves every ready word at n, so a consumer of that call waits for
  *    n.  Nothing needs to be cleared between calls.
+ *  - A chunk's send rows are written through the L2 to memory and have
+ *    completed before its ready word rises (an atomic add with device-scope
+ *    release), so a reader on this GPU that sees the word with a
+ *    device-scope acquire then reads the chunk's data.
  *  - Pointers are device pointers owned by the caller, 16-byte aligned; the
  *    output buffers (send_bufs, out, flags) must not overlap each other or
  *    the inputs.  Unused pointers may be NULL: peer_partials, send_bufs and
